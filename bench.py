@@ -1,0 +1,269 @@
+"""Throughput of the DSA forward on one MI355X (prints one JSON line).
+
+A step is one pass of the layer's forward hot path over the whole sequence: for every query
+chunk, indexer scores -> top-k -> sparse attention (dsa_forward_chunked).  Inputs are
+seeded synthetic tensors, resident on the GPU before timing starts.  `value` is tokens/s of
+the whole forward.  A second, instrumented pass calls the three entry points chunk by chunk
+with events between launches on the launching stream, which gives each kernel's average
+launch duration; from it come per-phase rates and the roofline fraction of the dominant
+kernel (algorithmic bytes or flops per launch / measured duration / MI355X peak).  The CPU
+oracle is timed on a bounded sample of rows of the same workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+DEFAULT_WORKLOAD = "fwd_128k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def chunk_ranges(n, chunk):
+    return [(t0, min(chunk, n - t0)) for t0 in range(0, n, chunk)]
+
+
+def visible_pairs(t0, nq, p):
+    """sum over t in [t0, t0 + nq) of min(p, floor((t + 1) / 4)), exactly."""
+    t = np.arange(t0, t0 + nq, dtype=np.int64)
+    return int(np.minimum(p, (t + 1) // 4).sum())
+
+
+def valid_slots(t0, nq, p, k):
+    t = np.arange(t0, t0 + nq, dtype=np.int64)
+    return int(np.minimum(k, np.minimum(p, (t + 1) // 4)).sum())
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_sparse_index_amd import binding as B
+    from long_context_sparse_index_amd import inputs as I
+    from long_context_sparse_index_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.load_library()
+    n, p, k, chunk = wl.n_tokens, wl.n_pools, wl.topk, wl.chunk
+    has_attn = wl.heads > 0
+    print("bench: workload %s (N=%d, P=%d, chunk %d)" % (wl.name, n, p, chunk),
+          file=sys.stderr, flush=True)
+
+    q_i, k_i, w = I.index_inputs(wl, dev)
+    ld = ((p + 3) // 4) * 4
+    if has_attn:
+        q, kv, _ = I.attn_inputs(wl, dev)
+        o = torch.empty((n, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
+        lse = torch.empty((n, wl.heads), dtype=torch.float32, device=dev)
+        ws = torch.empty(B.forward_chunked_workspace_bytes(p, chunk, k), dtype=torch.uint8,
+                         device=dev)
+    scores = torch.empty((chunk, ld), dtype=torch.float32, device=dev)
+    idx_chunk = torch.empty((chunk, k), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    chunks = chunk_ranges(n, chunk)
+
+    def step_driver():
+        B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=k, chunk=chunk, scale=wl.scale,
+                          d_v=wl.d_v, ws=ws)
+
+    def step_phases(events):
+        for t0, nq in chunks:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            B.index_scores(q_i[t0:t0 + nq], k_i, w, scores[:nq], q_start=t0)
+            e[1].record(stream)
+            B.topk(scores[:nq], idx_chunk[:nq], q_start=t0, n_pools=p)
+            e[2].record(stream)
+            if has_attn:
+                B.sparse_attn_fwd(q[t0:t0 + nq], kv, idx_chunk[:nq], o[t0:t0 + nq],
+                                  lse[t0:t0 + nq], scale=wl.scale, d_v=wl.d_v)
+            e[3].record(stream)
+            events.append((t0, nq, e))
+
+    step = step_driver if has_attn else (lambda: step_phases([]))
+
+    # ---- timed region: whole forward steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    print("bench: %.3f ms/step (wall %.3f s for %d steps)" % (ms_per_step, wall, args.steps),
+          file=sys.stderr, flush=True)
+
+    # ---- instrumented pass: per-kernel launch durations on the launching stream
+    events = []
+    for _ in range(args.steps):
+        step_phases(events)
+    torch.cuda.synchronize()
+    ph_ms = {"indexer": 0.0, "topk": 0.0, "attn_fwd": 0.0}
+    for _, _, e in events:
+        ph_ms["indexer"] += e[0].elapsed_time(e[1])
+        ph_ms["topk"] += e[1].elapsed_time(e[2])
+        ph_ms["attn_fwd"] += e[2].elapsed_time(e[3])
+    per_step = {kname: v / args.steps for kname, v in ph_ms.items()}
+    n_launch = len(chunks)
+
+    # algorithmic work of one step
+    pairs = visible_pairs(0, n, p)
+    idx_flop = 2.0 * wl.h_i * wl.d_i * pairs
+    topk_bytes = 4.0 * pairs + 4.0 * n * k
+    slots = valid_slots(0, n, p, k)
+    row_bytes = 2 * wl.d_qk if has_attn else 0
+    attn_bytes = (row_bytes * slots + n * wl.heads * wl.d_qk * 2 + n * wl.heads * wl.d_v * 4 +
+                  n * k * 4) if has_attn else 0.0
+    attn_flop = 2.0 * wl.heads * (wl.d_qk + wl.d_v) * slots if has_attn else 0.0
+    idx_peak = PEAK_FP8_TFLOPS if wl.index_dtype == "fp8" else PEAK_BF16_TFLOPS
+
+    def tflops(flop, ms):
+        return flop / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+
+    phases = {
+        "indexer": {"ms_per_step": per_step["indexer"], "launches_per_step": n_launch,
+                    "avg_launch_ms": per_step["indexer"] / n_launch,
+                    "tflops": tflops(idx_flop, per_step["indexer"]),
+                    "frac_of_mfma_peak": tflops(idx_flop, per_step["indexer"]) / idx_peak,
+                    "visible_pairs_per_s": pairs / (per_step["indexer"] * 1e-3),
+                    "tokens_per_s": n / (per_step["indexer"] * 1e-3)},
+        "topk": {"ms_per_step": per_step["topk"], "avg_launch_ms": per_step["topk"] / n_launch,
+                 "gbs": gbs(topk_bytes, per_step["topk"]),
+                 "frac_of_hbm_peak": gbs(topk_bytes, per_step["topk"]) / PEAK_HBM_GBS,
+                 "tokens_per_s": n / (per_step["topk"] * 1e-3)},
+    }
+    if has_attn:
+        phases["attn_fwd"] = {
+            "ms_per_step": per_step["attn_fwd"], "avg_launch_ms": per_step["attn_fwd"] / n_launch,
+            "gbs": gbs(attn_bytes, per_step["attn_fwd"]),
+            "frac_of_hbm_peak": gbs(attn_bytes, per_step["attn_fwd"]) / PEAK_HBM_GBS,
+            "tflops": tflops(attn_flop, per_step["attn_fwd"]),
+            "frac_of_mfma_peak": tflops(attn_flop, per_step["attn_fwd"]) / PEAK_BF16_TFLOPS,
+            "tokens_per_s": n / (per_step["attn_fwd"] * 1e-3)}
+
+    # roofline of the dominant kernel (largest share of the step)
+    dom = max(per_step, key=lambda x: per_step[x])
+    if dom == "indexer":
+        ach = tflops(idx_flop / n_launch, per_step["indexer"] / n_launch)
+        roof = {"kernel": "indexer", "bound": "mfma", "achieved": ach, "peak": idx_peak,
+                "unit": "TFLOP/s", "frac": ach / idx_peak, "traffic": None}
+    elif dom == "topk":
+        ach = gbs(topk_bytes / n_launch, per_step["topk"] / n_launch)
+        roof = {"kernel": "topk", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+    else:
+        ach = gbs(attn_bytes / n_launch, per_step["attn_fwd"] / n_launch)
+        roof = {"kernel": "attn_fwd", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, q_i, k_i, w, q if has_attn else None, kv if has_attn else None,
+                           args.cpu_seconds)
+
+    value = n / (ms_per_step * 1e-3)
+    line = {
+        "metric": "DSA forward tokens/s (indexer + top-k + sparse attention, chunked)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_tokens": n, "n_pools": p, "h_i": wl.h_i,
+                   "d_i": wl.d_i, "index_dtype": wl.index_dtype, "topk": k,
+                   "heads": wl.heads, "d_qk": wl.d_qk, "d_v": wl.d_v, "chunk": chunk,
+                   "attn_out": "fp32"},
+        "roofline": roof,
+        "phases": phases,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):
+    """The CPU oracle, as it stands, on uniformly sampled rows of the same workload; its
+    tokens/s is rows / seconds (a uniform sample has the workload's mean cost per row)."""
+    import torch
+
+    import oracle
+    from long_context_sparse_index_amd import inputs as I
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = min(threads, 16)
+    rng = np.random.default_rng(1234)
+    k_bits = I.index_bits(k_i)
+    kv_bits = I.bits_u16(kv) if kv is not None else None
+    w_h = w.cpu().numpy()
+
+    def run(nrows):
+        rows = np.sort(rng.choice(wl.n_tokens, size=nrows, replace=False)).astype(np.int64)
+        ridx = torch.from_numpy(rows).to(q_i.device)
+        q_rows = I.index_bits(q_i[ridx])
+        q_att = I.bits_u16(q[ridx]) if q is not None else None
+        t0 = time.perf_counter()
+        sc = oracle.index_scores(q_rows, k_bits, w_h, rows, wl.n_pools, threads=threads)
+        sel = oracle.topk(sc, rows, wl.n_pools, wl.topk, threads=threads)
+        if q is not None:
+            oracle.sparse_attn_fwd(q_att, kv_bits, sel, wl.scale, d_v=wl.d_v, threads=threads)
+        return time.perf_counter() - t0
+
+    nrows = 2 * threads
+    dt = run(nrows)
+    target = max(1, min(wl.n_tokens, int(nrows * budget_s / max(dt, 1e-3))))
+    if target > nrows:
+        nrows = target
+        dt = run(nrows)
+    return {"value": nrows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d uniformly sampled query rows of %s (seed 1234), all phases of the "
+                      "forward, %.1f s" % (nrows, wl.name, dt)}
+
+
+if __name__ == "__main__":
+    main()

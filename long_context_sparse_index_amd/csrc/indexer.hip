@@ -1,0 +1,295 @@
+// Lightning-indexer scores on gfx950 MFMA.
+//
+// Page "SkyRL extends GLM-5.3-Flash training context to 1 million tokens", section "Model and
+// bottleneck": every query scores every visible pooled key (one pool per 4 tokens), which is
+// the quadratic part of the layer.  Score I[t,s] = sum_j w[t,j] * max(0, q[t,j,:] . k[s,:]).
+//
+// Tiling.  A block owns a tile of BQ queries x 256 pools; each of its 4 waves owns 64 pools
+// and keeps their key rows in registers as MFMA A operands for the whole head loop, since
+// the pooled key is shared by all indexer heads.  The queries of one head are staged in LDS
+// (double-buffered, one barrier per head) and read by all waves as B operands.  Each head's
+// 16x16 products are ReLU'd and added with the head weight into fp32 score registers, so
+// the per-head products never leave the register file.  Products are laid out
+// pool-major (MFMA rows = pools, columns = queries), which puts one query per lane column:
+// the head weight is one value per lane and the finished scores go out as 16-byte rows.
+//
+// The grid covers the causal trapezoid: tiles whose first pool lies beyond the visible
+// prefix of the tile's last query exit at once.  Block ids are remapped so that the pool
+// tiles of one query tile run on the same XCD (blocks are dealt to the 8 XCDs round-robin)
+// and share the query tile through that XCD's L2.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int kIdxWaves = 4;
+constexpr int kIdxThreads = kIdxWaves * kWave;
+constexpr int kPoolsPerWave = 64;
+constexpr int kMB = kPoolsPerWave / 16;
+constexpr int kPoolsPerBlock = kIdxWaves * kPoolsPerWave;
+constexpr int kMaxHeads = 64;
+
+template <bool FP8>
+struct FragT;
+template <>
+struct FragT<false> {
+  using type = bf16x8;
+};
+template <>
+struct FragT<true> {
+  using type = i32x8;
+};
+
+template <bool FP8>
+__device__ __forceinline__ typename FragT<FP8>::type load_frag(const uint8_t* p) {
+  if constexpr (FP8) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  } else {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ typename FragT<FP8>::type zero_frag() {
+  typename FragT<FP8>::type z;
+  if constexpr (FP8) {
+    for (int i = 0; i < 8; ++i) z[i] = 0;
+  } else {
+    z = bf16x8_zero();
+  }
+  return z;
+}
+
+template <bool FP8>
+__device__ __forceinline__ f32x4 mfma_frag(typename FragT<FP8>::type a,
+                                           typename FragT<FP8>::type b, f32x4 c) {
+  if constexpr (FP8)
+    return mfma16x16x128_e4m3(a, b, c);
+  else
+    return mfma16x16x32_bf16(a, b, c);
+}
+
+// D: d_i; NB: 16-query column blocks per tile (BQ = 16 * NB); FP8: e4m3 operands.
+template <int D, int NB, bool FP8>
+__global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
+    const uint8_t* __restrict__ q, int64_t q_stride_b, const uint8_t* __restrict__ k,
+    int64_t k_stride_b, const float* __restrict__ w, int64_t w_stride,
+    float* __restrict__ scores, int64_t ld, int64_t q_start, int64_t nq, int64_t n_pools,
+    int h_i, int accumulate, int n_pool_tiles, int n_query_tiles) {
+  using Frag = typename FragT<FP8>::type;
+  constexpr int kRowBytes = D * (FP8 ? 1 : 2);
+  constexpr int kFragBytes = FP8 ? 32 : 16;        // bytes of one row per lane group
+  constexpr int kStepBytes = 4 * kFragBytes;       // bytes of one row per MFMA
+  constexpr int kKS = kRowBytes / kStepBytes;      // MFMAs per head per tile
+  constexpr int kBQ = 16 * NB;
+  constexpr int kLdsRow = kRowBytes + 16;          // padded LDS row of one query
+  constexpr int kChunksPerRow = kRowBytes / 16;
+  constexpr int kChunks = kBQ * kChunksPerRow;
+  constexpr int kChunksPerThread = (kChunks + kIdxThreads - 1) / kIdxThreads;
+  static_assert(kRowBytes % kStepBytes == 0, "d_i must fill whole MFMA steps");
+
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][kBQ * kLdsRow];
+  __shared__ float w_lds[kBQ * kMaxHeads];
+
+  // XCD-aware remap: consecutive logical tiles (same query tile) land on one XCD.
+  const int n_tiles = n_pool_tiles * n_query_tiles;
+  const int per_xcd = (n_tiles + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= n_tiles) return;
+  const int qt = logical / n_pool_tiles;
+  const int pt = logical - qt * n_pool_tiles;
+  const int64_t q0 = static_cast<int64_t>(qt) * kBQ;
+  const int64_t p0 = static_cast<int64_t>(pt) * kPoolsPerBlock;
+  const int64_t rows_here = (nq - q0) < kBQ ? (nq - q0) : kBQ;
+  const int64_t vis_last = visible_pools(q_start + q0 + rows_here - 1, n_pools);
+  if (p0 >= vis_last) return;  // whole tile above the causal boundary
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int64_t pw0 = p0 + wid * kPoolsPerWave;
+  const bool wave_live = pw0 < vis_last;
+
+  // Head weights of the tile's queries.
+  for (int i = tid; i < kBQ * h_i; i += kIdxThreads) {
+    const int row = i / h_i;
+    const int j = i - row * h_i;
+    w_lds[row * kMaxHeads + j] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
+  }
+
+  // This wave's pooled key rows, resident for all heads.
+  Frag kf[kMB][kKS];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) {
+    const int64_t pool = pw0 + mb * 16 + r16;
+    const bool ok = wave_live && pool < n_pools;
+    const uint8_t* kp = k + (ok ? pool : 0) * k_stride_b + g * kFragBytes;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      kf[mb][ks] = ok ? load_frag<FP8>(kp + ks * kStepBytes) : zero_frag<FP8>();
+  }
+
+  u32x4 pre[kChunksPerThread];
+  auto load_q = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerThread; ++c) {
+      const int chunk = tid + c * kIdxThreads;
+      const int row = chunk / kChunksPerRow;
+      const int col = chunk - row * kChunksPerRow;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (chunk < kChunks && q0 + row < nq)
+        v = *reinterpret_cast<const u32x4*>(q + (q0 + row) * q_stride_b +
+                                            static_cast<int64_t>(j) * kRowBytes + col * 16);
+      pre[c] = v;
+    }
+  };
+  auto store_q = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerThread; ++c) {
+      const int chunk = tid + c * kIdxThreads;
+      if (chunk < kChunks) {
+        const int row = chunk / kChunksPerRow;
+        const int col = chunk - row * kChunksPerRow;
+        *reinterpret_cast<u32x4*>(&q_lds[buf][row * kLdsRow + col * 16]) = pre[c];
+      }
+    }
+  };
+
+  f32x4 sc[kMB][NB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_q(0);
+  store_q(0);
+  __syncthreads();
+  for (int j = 0; j < h_i; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < h_i) load_q(j + 1);
+    if (wave_live) {
+      f32x4 acc[kMB][NB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        Frag qf[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          qf[nb] = load_frag<FP8>(&q_lds[buf][(nb * 16 + r16) * kLdsRow + ks * kStepBytes +
+                                              g * kFragBytes]);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb], acc[mb][nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float wv = w_lds[(nb * 16 + r16) * kMaxHeads + j];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[mb][nb][i] = __builtin_fmaf(wv, __builtin_fmaxf(acc[mb][nb][i], 0.0f),
+                                           sc[mb][nb][i]);
+      }
+    }
+    if (j + 1 < h_i) store_q(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live) return;
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t row = q0 + nb * 16 + r16;
+    if (row >= nq) continue;
+    const int64_t vis = visible_pools(q_start + row, n_pools);
+    float* dst_row = scores + row * ld;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int64_t p = pw0 + mb * 16 + g * 4;
+      f32x4 val = sc[mb][nb];
+      float* dst = dst_row + p;
+      if (p + 4 <= vis) {
+        if (accumulate) val += *reinterpret_cast<const f32x4*>(dst);
+        *reinterpret_cast<f32x4*>(dst) = val;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (p + i < vis) dst[i] = accumulate ? dst[i] + val[i] : val[i];
+      }
+    }
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
+                            int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                            float* scores, int64_t ld, int64_t q_start, int64_t nq,
+                            int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
+  constexpr int NB = 2;
+  constexpr int kBQ = 16 * NB;
+  const int64_t elt = FP8 ? 1 : 2;
+  const int64_t vis_max = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
+  if (nq <= 0 || vis_max <= 0) return hipSuccess;
+  const int64_t n_query_tiles = (nq + kBQ - 1) / kBQ;
+  const int64_t n_pool_tiles = (vis_max + kPoolsPerBlock - 1) / kPoolsPerBlock;
+  const int64_t n_tiles = n_query_tiles * n_pool_tiles;
+  if (n_tiles >= (int64_t{1} << 31) - 8) return hipErrorInvalidConfiguration;
+  const int64_t grid = ((n_tiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((indexer_kernel<D, NB, FP8>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kIdxThreads), 0, stream, static_cast<const uint8_t*>(q),
+                     q_row_stride * elt, static_cast<const uint8_t*>(k), k_row_stride * elt, w,
+                     w_row_stride, scores, ld, q_start, nq, n_pools, h_i, accumulate,
+                     static_cast<int>(n_pool_tiles), static_cast<int>(n_query_tiles));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_supported(int d_i, int dtype) {
+  if (dtype == 0) return d_i == 32 || d_i == 64 || d_i == 128 || d_i == 256;
+  if (dtype == 1) return d_i == 128 || d_i == 256;
+  return false;
+}
+
+int indexer_max_heads() { return kMaxHeads; }
+
+hipError_t launch_index_scores(const void* q, int64_t q_row_stride, const void* k,
+                               int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                               float* scores, int64_t ld, int64_t q_start, int64_t nq,
+                               int64_t n_pools, int h_i, int d_i, int dtype, int accumulate,
+                               hipStream_t stream) {
+#define DSA_IDX_CASE(DD, F8)                                                                 \
+  return launch_indexer_t<DD, F8>(q, q_row_stride, k, k_row_stride, w, w_row_stride, scores, \
+                                  ld, q_start, nq, n_pools, h_i, accumulate, stream)
+  if (dtype == 0) {
+    switch (d_i) {
+      case 32: DSA_IDX_CASE(32, false);
+      case 64: DSA_IDX_CASE(64, false);
+      case 128: DSA_IDX_CASE(128, false);
+      case 256: DSA_IDX_CASE(256, false);
+    }
+  } else if (dtype == 1) {
+    switch (d_i) {
+      case 128: DSA_IDX_CASE(128, true);
+      case 256: DSA_IDX_CASE(256, true);
+    }
+  }
+#undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

@@ -95,6 +95,24 @@ void parallel_rows(int64_t n, int nthreads, F body) {
   for (auto& th : pool) th.join();
 }
 
+// Runs body(i, w) for i in [0, n) with worker w taking the fixed contiguous block
+// [w * n / nt, (w + 1) * n / nt): the work each worker sees, and so any per-worker
+// floating-point accumulation, does not depend on thread timing.
+template <class F>
+void parallel_rows_static(int64_t n, int nt, F body) {
+  if (nt <= 1) {
+    for (int64_t i = 0; i < n; ++i) body(i, 0);
+    return;
+  }
+  std::vector<std::thread> pool;
+  for (int w = 0; w < nt; ++w)
+    pool.emplace_back([&, w] {
+      const int64_t lo = n * w / nt, hi = n * (w + 1) / nt;
+      for (int64_t i = lo; i < hi; ++i) body(i, w);
+    });
+  for (auto& th : pool) th.join();
+}
+
 // Decodes a table of `rows` rows of `cols` values with row stride `stride` (elements).
 std::vector<double> decode_table(const void* src, int dtype, int64_t rows, int64_t cols,
                                  int64_t stride) {
@@ -267,13 +285,13 @@ int attn_bwd(const AttnArgs& a, const double* d_o, double* dq, double* dk, doubl
   if (int rc = check_attn(a)) return rc;
   const int64_t n_pools = a.n_pools;
   const int nt = resolve_threads(nthreads, a.nrows * a.h);
-  // One private accumulator per worker, summed in worker order at the end.
+  // One private accumulator per worker (fixed row blocks), summed in worker order at the end.
   std::vector<std::vector<double>> part_k(nt), part_v(nt);
   for (int w = 0; w < nt; ++w) {
     part_k[w].assign(static_cast<size_t>(n_pools * a.d_qk), 0.0);
     if (dv) part_v[w].assign(static_cast<size_t>(n_pools * a.d_v), 0.0);
   }
-  parallel_rows(a.nrows * a.h, nt, [&](int64_t item, int w) {
+  parallel_rows_static(a.nrows * a.h, nt, [&](int64_t item, int w) {
     const int64_t r = item / a.h;
     const int hh = static_cast<int>(item % a.h);
     std::vector<int32_t> sel;

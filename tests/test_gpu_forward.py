@@ -1,0 +1,279 @@
+"""GPU parity of the forward path (indexer scores, top-k, sparse attention, chunked driver)
+against the CPU oracle, through the C ABI.  Scores and indices must match bit-exactly;
+attention outputs within max |err| <= 2e-2 RMS and mean |err| <= 2e-3 RMS."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_index_amd import binding as B
+from long_context_sparse_index_amd import inputs as I
+from long_context_sparse_index_amd import workloads as W
+
+from gpu_util import assert_close, f32_bits_equal, host_bits, say
+
+pytestmark = pytest.mark.gpu
+TINY = W.WORKLOADS["tiny_4k"]
+
+
+def _visible(t, p):
+    return min(p, (t + 1) // 4)
+
+
+def _check_scores(gpu_scores, ref, rows, p, sentinel_untouched=True):
+    g = gpu_scores.cpu().numpy()
+    for r, t in enumerate(rows):
+        v = _visible(int(t), p)
+        assert f32_bits_equal(g[r, :v], ref[r, :v]), "row %d (t=%d) differs" % (r, t)
+        if sentinel_untouched:
+            assert np.all(np.isnan(g[r, v:p])), "row %d wrote beyond its visible prefix" % r
+
+
+def test_indexer_tiny_full_bit_exact(gpu):
+    say("case: indexer tiny_4k full")
+    q, k, w = I.index_inputs(TINY, gpu)
+    scores = B.index_scores_new(q, k, w)
+    torch.cuda.synchronize()
+    rows = np.arange(TINY.n_tokens)
+    ref = oracle.index_scores(host_bits(q), host_bits(k), w.cpu().numpy(), rows, TINY.n_pools)
+    _check_scores(scores, ref, rows, TINY.n_pools)
+
+
+@pytest.mark.parametrize("d_i", [32, 64, 128, 256])
+def test_indexer_ragged_offsets_negative_weights_accumulate(gpu, d_i):
+    say("case: indexer ragged d_i=%d" % d_i)
+    nq, q_start, p, h_i, ld = 777, 1234, 301, 5, 304
+    g = torch.Generator(device=gpu).manual_seed(7 + d_i)
+    q = torch.randint(-4, 5, (nq, h_i, d_i), generator=g, device=gpu, dtype=torch.int8).to(
+        torch.bfloat16)
+    k = torch.randint(-4, 5, (p, d_i), generator=g, device=gpu, dtype=torch.int8).to(
+        torch.bfloat16)
+    choices = torch.tensor([1.0, 0.5, -0.25, 2.0, 0.0], device=gpu)
+    w = choices[torch.randint(0, 5, (nq, h_i), generator=g, device=gpu)].float().contiguous()
+    scores = torch.full((nq, ld), float("nan"), device=gpu)
+    # heads 0..2 written, heads 3..4 accumulated on top (a head-share partial sum)
+    B.index_scores(q[:, :3], k, w[:, :3], scores, q_start=q_start)
+    B.index_scores(q[:, 3:], k, w[:, 3:], scores, q_start=q_start, accumulate=True)
+    torch.cuda.synchronize()
+    rows = np.arange(q_start, q_start + nq)
+    ref = oracle.index_scores(host_bits(q), host_bits(k), w.cpu().numpy(), rows, p)
+    _check_scores(scores, ref, rows, p)
+
+
+def test_indexer_fp8_bit_exact(gpu):
+    say("case: indexer fp8 e4m3, d_i=128")
+    wl = W.Workload(name="fp8_small", n_tokens=3000, n_pools=750, h_i=6, d_i=128,
+                    index_dtype="fp8", int_range=8, w_period=4, topk=64)
+    q, k, w = I.index_inputs(wl, gpu, seed=3)
+    scores = B.index_scores_new(q, k, w)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.n_tokens)
+    ref = oracle.index_scores(host_bits(q), host_bits(k), w.cpu().numpy(), rows, wl.n_pools)
+    _check_scores(scores, ref, rows, wl.n_pools)
+
+
+def test_topk_tiny_bit_exact(gpu):
+    say("case: topk tiny_4k")
+    q, k, w = I.index_inputs(TINY, gpu)
+    scores = B.index_scores_new(q, k, w)
+    idx = B.topk_new(scores, q_start=0, n_pools=TINY.n_pools, k=TINY.topk)
+    torch.cuda.synchronize()
+    rows = np.arange(TINY.n_tokens)
+    ref = oracle.topk(scores.cpu().numpy(), rows, TINY.n_pools, TINY.topk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    assert int((idx == -1).sum()) == 131328
+
+
+def _edge_scores(kind, nq, ld, rng):
+    if kind == "ties":
+        return np.zeros((nq, ld), np.float32)
+    if kind == "few_values":
+        return (rng.integers(0, 6, size=(nq, ld)) / 8.0).astype(np.float32)
+    if kind == "signed_zero_neg":
+        s = rng.choice(np.array([0.0, -0.0, -1.5, 2.0, -3e-38, 1e30], np.float32), size=(nq, ld))
+        return s.astype(np.float32)
+    if kind == "normal":
+        return rng.normal(size=(nq, ld)).astype(np.float32)
+    if kind == "clustered_ints":
+        return (rng.normal(450, 130, size=(nq, ld)).round() / 8.0).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["ties", "few_values", "signed_zero_neg", "normal",
+                                  "clustered_ints"])
+@pytest.mark.parametrize("k", [1, 100, 2048, 2051, 4096])
+def test_topk_edge_cases(gpu, kind, k):
+    say("case: topk edge kind=%s k=%d" % (kind, k))
+    rng = np.random.default_rng(zlib.crc32(("%s/%d" % (kind, k)).encode()))
+    p = 20000
+    ld = 20000
+    rows = np.array([0, 1, 2, 3, 7, 4 * k - 2, 4 * k - 1, 4 * k, 4 * k + 5, 30011, 79999,
+                     4 * p + 9], dtype=np.int64)
+    host = _edge_scores(kind, len(rows), ld, rng)
+    scores = torch.from_numpy(host).to(gpu)
+    idx = torch.empty((len(rows), k), dtype=torch.int32, device=gpu)
+    # rows are not consecutive: run one call per row with its own q_start
+    for r, t in enumerate(rows):
+        B.topk(scores[r:r + 1], idx[r:r + 1], q_start=int(t), n_pools=p)
+    torch.cuda.synchronize()
+    ref = oracle.topk(host, rows, p, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_chunk_of_consecutive_rows(gpu):
+    say("case: topk consecutive rows, clustered ints, q_start=100000")
+    rng = np.random.default_rng(5)
+    p, nq, k, q_start = 32768, 256, 2048, 100000
+    host = _edge_scores("clustered_ints", nq, p, rng)
+    scores = torch.from_numpy(host).to(gpu)
+    idx = B.topk_new(scores, q_start=q_start, n_pools=p, k=k)
+    torch.cuda.synchronize()
+    ref = oracle.topk(host, np.arange(q_start, q_start + nq), p, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def _attn_ref(q, kv, idx, scale, d_v, v=None):
+    return oracle.sparse_attn_fwd(host_bits(q), host_bits(kv), idx.cpu().numpy(), scale,
+                                  v_bits=None if v is None else host_bits(v), d_v=d_v)
+
+
+@pytest.mark.parametrize("separate_v", [False, True])
+def test_attention_tiny(gpu, separate_v):
+    say("case: attention tiny_4k separate_v=%s" % separate_v)
+    q_i, k_i, w = I.index_inputs(TINY, gpu)
+    idx = B.topk_new(B.index_scores_new(q_i, k_i, w), q_start=0, n_pools=TINY.n_pools,
+                     k=TINY.topk)
+    q, kv, v = I.attn_inputs(TINY, gpu, separate_v=separate_v)
+    o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=TINY.scale, d_v=TINY.d_v, v=v)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(q, kv, idx, TINY.scale, TINY.d_v, v)
+    assert_close(o.cpu().numpy(), ro, "O")
+    lse_h = lse.cpu().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse_h), fin)
+    assert np.all(o.cpu().numpy()[:3] == 0.0)
+    assert np.max(np.abs(lse_h[fin] - rl[fin])) < 1e-4
+
+
+def test_attention_bf16_output_is_correctly_rounded(gpu):
+    say("case: attention tiny_4k, bf16 output")
+    q_i, k_i, w = I.index_inputs(TINY, gpu)
+    idx = B.topk_new(B.index_scores_new(q_i, k_i, w), q_start=0, n_pools=TINY.n_pools,
+                     k=TINY.topk)
+    q, kv, _ = I.attn_inputs(TINY, gpu)
+    o, _ = B.sparse_attn_fwd_new(q, kv, idx, scale=TINY.scale, d_v=TINY.d_v,
+                                 out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, _ = _attn_ref(q, kv, idx, TINY.scale, TINY.d_v)
+    got = o.float().cpu().numpy()
+    # bf16 round-to-nearest-even moves a value by at most 2^-8 of its magnitude; allow that
+    # plus a small absolute term for the fp32 path before the rounding.
+    rms = float(np.sqrt(np.mean(ro * ro)))
+    excess = np.abs(got - ro) - (2.0 ** -8 * np.abs(ro) + 1e-4 * rms)
+    say("  worst excess over the bf16 rounding bound: %.3g (rms %.3g)" % (excess.max(), rms))
+    assert excess.max() <= 0.0
+
+
+@pytest.mark.parametrize("h", [64, 40, 16, 5])
+def test_attention_latent_576_random_selection(gpu, h):
+    say("case: attention 576/512 random idx h=%d" % h)
+    nq, p, k = 48, 4096, 2048
+    g = torch.Generator(device=gpu).manual_seed(11 + h)
+    q = torch.randn((nq, h, 576), generator=g, device=gpu, dtype=torch.bfloat16)
+    kv = torch.randn((p, 576), generator=g, device=gpu, dtype=torch.bfloat16)
+    perm = torch.argsort(torch.rand((nq, p), generator=g, device=gpu), dim=1)[:, :k]
+    idx = perm.to(torch.int32).contiguous()
+    drop = torch.rand((nq, k), generator=g, device=gpu) < 0.1
+    idx[drop] = -1
+    idx[0] = -1  # a row with no valid slot
+    idx[1, :] = -1
+    idx[1, 5] = 17  # a row with one valid slot
+    idx[2, 33:] = -1  # a partial last tile
+    scale = 1.0 / 24.0
+    o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=scale, d_v=512)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(q, kv, idx, scale, 512)
+    assert_close(o.cpu().numpy(), ro, "O")
+    lse_h = lse.cpu().numpy()
+    assert np.all(np.isneginf(lse_h[0])) and np.all(o[0].cpu().numpy() == 0)
+    assert np.array_equal(o[1].cpu().numpy(), np.broadcast_to(
+        kv[17, :512].float().cpu().numpy(), (h, 512)))  # one slot: O is that value row
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(lse_h[fin] - rl[fin])) < 1e-4
+
+
+def test_chunked_matches_separate_calls_and_is_chunk_invariant(gpu):
+    say("case: forward_chunked tiny_4k, chunks 4096/1000/7")
+    q_i, k_i, w = I.index_inputs(TINY, gpu)
+    q, kv, _ = I.attn_inputs(TINY, gpu)
+    n = TINY.n_tokens
+    outs = []
+    for chunk in (4096, 1000, 7):
+        o = torch.empty((n, TINY.heads, TINY.d_v), dtype=torch.float32, device=gpu)
+        lse = torch.empty((n, TINY.heads), dtype=torch.float32, device=gpu)
+        idx = torch.empty((n, TINY.topk), dtype=torch.int32, device=gpu)
+        B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=TINY.topk, chunk=chunk,
+                          scale=TINY.scale, d_v=TINY.d_v, idx_out=idx)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu(), idx.cpu()))
+    for o, lse, idx in outs[1:]:
+        assert torch.equal(idx, outs[0][2])
+        assert torch.equal(o.view(torch.int32), outs[0][0].view(torch.int32))
+        assert torch.equal(lse, outs[0][1])
+    rows = np.arange(n)
+    ref_idx = oracle.topk(oracle.index_scores(host_bits(q_i), host_bits(k_i), w.cpu().numpy(),
+                                              rows, TINY.n_pools), rows, TINY.n_pools, TINY.topk)
+    assert np.array_equal(outs[0][2].numpy(), ref_idx)
+    ro, _ = oracle.sparse_attn_fwd(host_bits(q), host_bits(kv), ref_idx, TINY.scale)
+    assert_close(outs[0][0].numpy(), ro, "O")
+
+
+def _full_size_forward(gpu, wl, check_rows):
+    q_i, k_i, w = I.index_inputs(wl, gpu)
+    q, kv, _ = I.attn_inputs(wl, gpu)
+    n = wl.n_tokens
+    o = torch.empty((n, wl.heads, wl.d_v), dtype=torch.float32, device=gpu)
+    lse = torch.empty((n, wl.heads), dtype=torch.float32, device=gpu)
+    idx = torch.empty((n, wl.topk), dtype=torch.int32, device=gpu)
+    B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=wl.topk, chunk=wl.chunk, scale=wl.scale,
+                      d_v=wl.d_v, idx_out=idx)
+    torch.cuda.synchronize()
+    say("  forward done")
+    # structural invariants on every row
+    t = torch.arange(n, device=gpu, dtype=torch.int64)
+    vis = torch.clamp((t + 1) // 4, max=wl.n_pools)
+    c = torch.clamp(vis, max=wl.topk)
+    valid = idx >= 0
+    assert torch.equal(valid.sum(1), c)
+    slot = torch.arange(wl.topk, device=gpu)
+    assert torch.equal(valid, slot[None, :] < c[:, None])  # valid slots first
+    assert bool((idx.long() < vis[:, None]).all())
+    srt = torch.sort(idx, dim=1).values
+    dup = (srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] >= 0)
+    assert not bool(dup.any())
+    say("  structure ok on all %d rows" % n)
+    # sampled rows against the oracle
+    rows = check_rows
+    q_rows = host_bits(q_i[torch.from_numpy(rows).to(gpu)])
+    ref_scores = oracle.index_scores(q_rows, host_bits(k_i), w.cpu().numpy(), rows, wl.n_pools)
+    ref_idx = oracle.topk(ref_scores, rows, wl.n_pools, wl.topk)
+    got_idx = idx[torch.from_numpy(rows).to(gpu)].cpu().numpy()
+    assert np.array_equal(got_idx, ref_idx)
+    say("  idx bit-exact on %d sampled rows" % len(rows))
+    ro, rl = oracle.sparse_attn_fwd(host_bits(q[torch.from_numpy(rows).to(gpu)]),
+                                    host_bits(kv), ref_idx, wl.scale, d_v=wl.d_v)
+    got_o = o[torch.from_numpy(rows).to(gpu)].cpu().numpy()
+    assert_close(got_o, ro, "O (sampled rows)")
+    got_l = lse[torch.from_numpy(rows).to(gpu)].cpu().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.max(np.abs(got_l[fin] - rl[fin])) < 1e-4
+
+
+def test_fwd_128k_full_size_sampled(gpu):
+    wl = W.WORKLOADS["fwd_128k"]
+    say("case: fwd_128k full size (N=%d), chunk %d" % (wl.n_tokens, wl.chunk))
+    _full_size_forward(gpu, wl, I.sample_rows(wl, n_uniform=24))
