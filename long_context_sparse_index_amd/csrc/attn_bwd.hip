@@ -1,18 +1,438 @@
-// Sparse MQA attention backward (placeholder until the kernels land).
-#include "common.hpp"
+// Backward of the sparse MQA attention, on gfx950 MFMA with fp32 atomics for dK/dV.
+//
+// The pages train the layer (page "SkyRL extends GLM-5.3-Flash training context to 1 million
+// tokens", from the title on) but print no backward; this is the exact gradient of the
+// forward in attn_fwd.hip.  With P = exp(scale q.K - LSE), dP = dO.V, D = dO.O and
+// dS = P (dP - D):
+//     dQ = scale dS K,   dK[idx] += scale dS^T q,   dV[idx] += P^T dO.
+//
+// Three launches on the caller's stream:
+//   1. delta: D[t, h] = dO[t, h, :] . O[t, h, :], one wave per (token, head) row.
+//   2. dq: per token, one wave per 16 heads, over 32-key tiles of the gathered latent rows:
+//      recompute S^T and P^T as the forward does, dP^T = V_tile . dO^T (A: value rows from
+//      LDS, B: the wave's dO, held in registers), dS^T in registers, and
+//      dQ^T += K_tile^T . dS^T with K^T from LDS transpose reads; dQ stays in registers.
+//   3. dkv: per token, the same recomputation, then P^T and dS^T of all 64 heads go to LDS
+//      and each wave forms its quarter of the tile's columns of
+//          dK_tile = dS^T . Q (contraction over the 64 heads),  dV_tile = P^T . dO
+//      so every (selected row, column) gets one fp32 atomic add per token, with the head
+//      sum already done in the MFMA.  The Q and dO operands for that product (heads along
+//      the contraction) are built once per token from LDS-staged copies with transpose
+//      reads.  With V aliased to the first d_v columns of the latent row and no separate
+//      dV buffer, the two contributions are added before the single atomic.
+// Probabilities and dS enter the MFMAs as bf16 hi + lo pairs (about 16 significant bits).
+// Summation order of the atomics varies from run to run.
+
+#include "attn_common.hpp"
 #include "launch.hpp"
 
 namespace dsa {
+namespace {
+
+// ---------------------------------------------------------------- 1. D = rowsum(dO * O)
+template <int DV, bool O_F32>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const void* __restrict__ o,
+                                                             const uint16_t* __restrict__ d_o,
+                                                             float* __restrict__ delta,
+                                                             int64_t n_rows) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  float acc = 0.0f;
+  for (int e = lane * 8; e < DV; e += 512) {
+    const u32x4 dv4 = *reinterpret_cast<const u32x4*>(d_o + r * DV + e);
+    float ov[8];
+    if constexpr (O_F32) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + r * DV + e);
+      const f32x4 b =
+          *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + r * DV + e + 4);
+      for (int i = 0; i < 4; ++i) ov[i] = a[i], ov[4 + i] = b[i];
+    } else {
+      const u32x4 a =
+          *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + r * DV + e);
+      for (int i = 0; i < 4; ++i) {
+        ov[2 * i] = __uint_as_float(a[i] << 16);
+        ov[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+      }
+    }
+    for (int i = 0; i < 4; ++i) {
+      acc += __uint_as_float(dv4[i] << 16) * ov[2 * i];
+      acc += __uint_as_float(dv4[i] & 0xFFFF0000u) * ov[2 * i + 1];
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+  if (lane == 0) delta[r] = acc;
+}
+
+// Per-tile recomputation shared by the dq and dkv kernels: S^T, P^T, dP^T and dS^T of the
+// wave's 16 heads for the 32 keys of the tile.  Probabilities and dS come back as bf16
+// hi/lo operand pairs in the S^T slot order (slot 4 mb + i <-> key 16 mb + 4 g + i).
+struct TileGrads {
+  bf16x8 p_hi, p_lo, ds_hi, ds_lo;
+  float p[2][4], ds[2][4];
+};
+
+template <int DQK, int DV, int VBASE>
+__device__ __forceinline__ void tile_grads(const uint8_t* tile, const bf16x8* qf,
+                                           const bf16x8* dof, int slot0, int n_valid,
+                                           bool head_ok, float scale_log2, float lse2,
+                                           float dh, int g, int r16, TileGrads& out) {
+  constexpr int kKS = DQK / 32;
+  constexpr int kVS = DV / 32;
+  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      s[mb] = mfma16x16x32_bf16(
+          *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]), qf[ks],
+          s[mb]);
+#pragma unroll
+  for (int ks = 0; ks < kVS; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      dp[mb] = mfma16x16x32_bf16(
+          *reinterpret_cast<const bf16x8*>(&tile[tile_off(VBASE + 4 * ks + g, mb * 16 + r16)]),
+          dof[ks], dp[mb]);
+  i16x8 ph, pl, sh, sl;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = head_ok && slot0 + mb * 16 + 4 * g + i < n_valid;
+      const float p = ok ? __builtin_exp2f(s[mb][i] * scale_log2 - lse2) : 0.0f;
+      const float d = p * (dp[mb][i] - dh);
+      out.p[mb][i] = p;
+      out.ds[mb][i] = d;
+      const uint16_t phb = float_to_bf16_bits(p);
+      const uint16_t shb = float_to_bf16_bits(d);
+      ph[mb * 4 + i] = static_cast<short>(phb);
+      pl[mb * 4 + i] = static_cast<short>(float_to_bf16_bits(p - bf16_bits_to_float(phb)));
+      sh[mb * 4 + i] = static_cast<short>(shb);
+      sl[mb * 4 + i] = static_cast<short>(float_to_bf16_bits(d - bf16_bits_to_float(shb)));
+    }
+  out.p_hi = bf16x8_from_bits(ph);
+  out.p_lo = bf16x8_from_bits(pl);
+  out.ds_hi = bf16x8_from_bits(sh);
+  out.ds_lo = bf16x8_from_bits(sl);
+}
+
+// The wave's B operands for S^T (queries) and dP^T (dO): lane column = head.
+template <int DQK, int DV>
+__device__ __forceinline__ void load_head_operands(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ d_o,
+                                                   int64_t row, int h, int head, bool head_ok,
+                                                   int g, bf16x8* qf, bf16x8* dof) {
+  const uint16_t* qrow = q + (row * h + (head_ok ? head : 0)) * DQK + g * 8;
+  const uint16_t* drow = d_o + (row * h + (head_ok ? head : 0)) * DV + g * 8;
+#pragma unroll
+  for (int ks = 0; ks < DQK / 32; ++ks)
+    qf[ks] = head_ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32) : bf16x8_zero();
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks)
+    dof[ks] = head_ok ? *reinterpret_cast<const bf16x8*>(drow + ks * 32) : bf16x8_zero();
+}
+
+// ---------------------------------------------------------------- 2. dQ
+template <int DQK, int DV, bool SEPARATE_V>
+__global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
+    const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
+    const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ delta, float* __restrict__ dq, int64_t n_pools, int h,
+    float scale_log2, float scale) {
+  using Gather = TileGather<DQK, DV, SEPARATE_V>;
+  constexpr int kNQ = DQK / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[Gather::kTileBytes];
+  __shared__ int32_t sel[kMaxTopK];
+  __shared__ int wave_tmp[kAttnThreads / 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int64_t row = blockIdx.x;
+  const int head = wid * 16 + r16;
+  const bool head_ok = head < h;
+  const bool wave_has_heads = wid * 16 < h;
+
+  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
+  bf16x8 qf[DQK / 32], dof[DV / 32];
+  load_head_operands<DQK, DV>(q, d_o, row, h, head, head_ok, g, qf, dof);
+  const float lse2 = head_ok && n_valid > 0 ? lse[row * h + head] * kLog2e : 0.0f;
+  const float dh = head_ok ? delta[row * h + head] : 0.0f;
+
+  f32x4 acc[kNQ];
+#pragma unroll
+  for (int nb = 0; nb < kNQ; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
+  Gather gather;
+  if (n_tiles > 0) gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();
+    gather.store(tile);
+    __syncthreads();
+    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
+    if (!wave_has_heads) continue;
+    TileGrads tg;
+    tile_grads<DQK, DV, Gather::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
+                                        scale_log2, lse2, dh, g, r16, tg);
+    // dQ^T += K^T . dS^T over the tile's keys.
+#pragma unroll
+    for (int nb = 0; nb < kNQ; ++nb) {
+      const bf16x8 kt = tile_cols_transposed(tile, 0, nb, g, r16);
+      acc[nb] = mfma16x16x32_bf16(kt, tg.ds_hi, acc[nb]);
+      acc[nb] = mfma16x16x32_bf16(kt, tg.ds_lo, acc[nb]);
+    }
+  }
+  if (!head_ok) return;
+  float* out = dq + (row * h + head) * DQK;
+#pragma unroll
+  for (int nb = 0; nb < kNQ; ++nb)
+    *reinterpret_cast<f32x4*>(out + nb * 16 + 4 * g) = acc[nb] * scale;
+}
+
+// ---------------------------------------------------------------- 3. dK, dV
+constexpr int kHeadsPad = 64;       // heads of the LDS-staged operands (zero beyond h)
+constexpr int kPsRow = kHeadsPad + 8;  // bf16 per key row of the P / dS arrays (padded)
+
+template <int DQK, int DV, bool SEPARATE_V>
+struct DkvLds {
+  using Gather = TileGather<DQK, DV, SEPARATE_V>;
+  static constexpr int kStageQ = kHeadsPad * (DQK + 8) * 2;
+  static constexpr int kStageO = kHeadsPad * (DV + 8) * 2;
+  static constexpr int kShared0 = kStageQ > kStageO ? kStageQ : kStageO;
+  static constexpr int kShared = kShared0 > Gather::kTileBytes ? kShared0 : Gather::kTileBytes;
+};
+
+// B operand for a product contracting over heads: lane (g, r) gets X[32 ks + 8 g + s][col0 + r]
+// for s = 0..7 from a row-major LDS copy X[head][col] with row stride `ld` elements.
+__device__ __forceinline__ bf16x8 heads_operand(const uint16_t* x, int ld, int ks, int col0,
+                                                int g, int r16) {
+  const int hrow = 32 * ks + 8 * g + (r16 >> 2);
+  const int col = col0 + 4 * (r16 & 3);
+  const i16x4 lo = lds_read_tr16(x + hrow * ld + col);
+  const i16x4 hi = lds_read_tr16(x + (hrow + 4) * ld + col);
+  return join_tr(lo, hi);
+}
+
+template <int DQK, int DV, bool SEPARATE_V>
+__global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
+    const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
+    const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ delta, float* __restrict__ dkv, float* __restrict__ dv,
+    int64_t n_pools, int h, float scale_log2, float scale) {
+  using Lds = DkvLds<DQK, DV, SEPARATE_V>;
+  using Gather = typename Lds::Gather;
+  constexpr int kCols = DQK / 4;     // output columns owned by each wave
+  constexpr int kNBW = kCols / 16;
+  static_assert(kCols % 16 == 0, "column split");
+  __shared__ __attribute__((aligned(16))) uint8_t shared[Lds::kShared];  // staging, then tiles
+  __shared__ __attribute__((aligned(16))) uint16_t ps[4][kKeysPerTile * kPsRow];
+  __shared__ int32_t sel[kMaxTopK];
+  __shared__ int wave_tmp[kAttnThreads / 64];
+  uint8_t* tile = shared;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(shared);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int64_t row = blockIdx.x;
+  const int head = wid * 16 + r16;
+  const bool head_ok = head < h;
+  const bool wave_has_heads = wid * 16 < h;
+  const int col_base = wid * kCols;
+
+  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
+  if (n_valid == 0) return;  // uniform: no selected row receives anything from this token
+
+  // Operands with heads along the contraction, for this wave's columns: Q, then dO.
+  bf16x8 qb[kNBW][2], db[kNBW][2];
+  {
+    constexpr int ld = DQK + 8;
+    for (int i = tid; i < kHeadsPad * (DQK / 8); i += kAttnThreads) {
+      const int hh = i / (DQK / 8), c = i - hh * (DQK / 8);
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (hh < h) val = *reinterpret_cast<const u32x4*>(q + (row * h + hh) * DQK + 8 * c);
+      *reinterpret_cast<u32x4*>(stage + hh * ld + 8 * c) = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        qb[nb][ks] = heads_operand(stage, ld, ks, col_base + 16 * nb, g, r16);
+    __syncthreads();
+  }
+  {
+    constexpr int ld = DV + 8;
+    for (int i = tid; i < kHeadsPad * (DV / 8); i += kAttnThreads) {
+      const int hh = i / (DV / 8), c = i - hh * (DV / 8);
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (hh < h) val = *reinterpret_cast<const u32x4*>(d_o + (row * h + hh) * DV + 8 * c);
+      *reinterpret_cast<u32x4*>(stage + hh * ld + 8 * c) = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        db[nb][ks] = col_base + 16 * nb < DV
+                         ? heads_operand(stage, ld, ks, col_base + 16 * nb, g, r16)
+                         : bf16x8_zero();
+  }
+
+  bf16x8 qf[DQK / 32], dof[DV / 32];
+  load_head_operands<DQK, DV>(q, d_o, row, h, head, head_ok, g, qf, dof);
+  const float lse2 = head_ok ? lse[row * h + head] * kLog2e : 0.0f;
+  const float dh = head_ok ? delta[row * h + head] : 0.0f;
+  const bool fold_v = dv == nullptr;  // V aliased and its gradient folded into dkv
+
+  const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
+  Gather gather;
+  gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();  // staging reads / previous tile and P, dS arrays fully consumed
+    gather.store(tile);
+    __syncthreads();
+    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
+    const int slot0 = t * kKeysPerTile;
+    TileGrads tg;
+    if (wave_has_heads) {
+      tile_grads<DQK, DV, Gather::kVBase>(tile, qf, dof, slot0, n_valid, head_ok, scale_log2,
+                                          lse2, dh, g, r16, tg);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tg.p[mb][i] = tg.ds[mb][i] = 0.0f;
+    }
+    // P^T and dS^T of this wave's heads into the [key][head] arrays (hi, lo parts).
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int at = (mb * 16 + 4 * g + i) * kPsRow + head;
+        const float p = tg.p[mb][i], d = tg.ds[mb][i];
+        const uint16_t phb = float_to_bf16_bits(p), shb = float_to_bf16_bits(d);
+        ps[0][at] = phb;
+        ps[1][at] = float_to_bf16_bits(p - bf16_bits_to_float(phb));
+        ps[2][at] = shb;
+        ps[3][at] = float_to_bf16_bits(d - bf16_bits_to_float(shb));
+      }
+    __syncthreads();
+    // This wave's columns of dK_tile = dS^T . Q and dV_tile = P^T . dO (64-head contraction).
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      bf16x8 a[4][2];
+#pragma unroll
+      for (int arr = 0; arr < 4; ++arr)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          a[arr][ks] = *reinterpret_cast<const bf16x8*>(
+              &ps[arr][(mb * 16 + r16) * kPsRow + 32 * ks + 8 * g]);
+      int32_t dst[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = slot0 + mb * 16 + 4 * g + i;
+        dst[i] = slot < n_valid ? sel[slot] : -1;
+      }
+#pragma unroll
+      for (int nb = 0; nb < kNBW; ++nb) {
+        const int col0 = col_base + 16 * nb;
+        f32x4 ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          ak = mfma16x16x32_bf16(a[2][ks], qb[nb][ks], ak);
+          ak = mfma16x16x32_bf16(a[3][ks], qb[nb][ks], ak);
+        }
+        f32x4 av = {0.f, 0.f, 0.f, 0.f};
+        if (col0 < DV) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            av = mfma16x16x32_bf16(a[0][ks], db[nb][ks], av);
+            av = mfma16x16x32_bf16(a[1][ks], db[nb][ks], av);
+          }
+        }
+        const int col = col0 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (dst[i] < 0) continue;
+          float* krow = dkv + static_cast<int64_t>(dst[i]) * DQK;
+          if (fold_v) {
+            atomicAdd(krow + col, ak[i] * scale + (col0 < DV ? av[i] : 0.0f));
+          } else {
+            atomicAdd(krow + col, ak[i] * scale);
+            if (col0 < DV) atomicAdd(dv + static_cast<int64_t>(dst[i]) * DV + col, av[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int DQK, int DV, bool SEP>
+hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void* v,
+                        int64_t ld_v, const int32_t* idx, int k, const void* o, int o_f32,
+                        const float* lse, const void* d_o, float* dq, float* dkv, float* dv,
+                        int64_t nq, int64_t n_pools, int h, float scale, float* delta,
+                        hipStream_t stream) {
+  const int64_t rows = nq * h;
+  const unsigned dgrid = static_cast<unsigned>((rows + 3) / 4);
+  if (o_f32)
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<DV, true>), dim3(dgrid), dim3(256), 0, stream, o,
+                       static_cast<const uint16_t*>(d_o), delta, rows);
+  else
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<DV, false>), dim3(dgrid), dim3(256), 0, stream, o,
+                       static_cast<const uint16_t*>(d_o), delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float sl2 = scale * kLog2e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, SEP>), dim3(static_cast<unsigned>(nq)),
+                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
+                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta, dq, n_pools, h,
+                     sl2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP>), dim3(static_cast<unsigned>(nq)),
+                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
+                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta, dkv, dv,
+                     n_pools, h, sl2, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 size_t attn_bwd_workspace_bytes(int64_t nq, int h) {
   return static_cast<size_t>(nq > 0 ? nq : 0) * static_cast<size_t>(h > 0 ? h : 0) * sizeof(float);
 }
 
-hipError_t launch_sparse_attn_bwd(const void*, const void*, int64_t, const void*, int64_t,
-                                  const int32_t*, int, const void*, int, const float*, const void*,
-                                  float*, float*, float*, int64_t, int64_t, int, int, int, float,
-                                  void*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
+                                  int64_t ld_v, const int32_t* idx, int k, const void* o,
+                                  int o_f32, const float* lse, const void* d_o, float* dq,
+                                  float* dkv, float* dv, int64_t nq, int64_t n_pools, int h,
+                                  int d_qk, int d_v, float scale, void* ws,
+                                  hipStream_t stream) {
+  if (nq <= 0) return hipSuccess;
+  if (nq * h >= (int64_t{1} << 33)) return hipErrorInvalidConfiguration;
+  float* delta = static_cast<float*>(ws);
+#define DSA_BWD(DQ, DVV)                                                                      \
+  return v ? launch_bwd_t<DQ, DVV, true>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, d_o,   \
+                                         dq, dkv, dv, nq, n_pools, h, scale, delta, stream)   \
+           : launch_bwd_t<DQ, DVV, false>(q, kv, ld_kv, nullptr, 0, idx, k, o, o_f32, lse,    \
+                                          d_o, dq, dkv, dv, nq, n_pools, h, scale, delta,     \
+                                          stream)
+  if (d_qk == 128 && d_v == 128) DSA_BWD(128, 128);
+  if (d_qk == 576 && d_v == 512) DSA_BWD(576, 512);
+#undef DSA_BWD
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dsa

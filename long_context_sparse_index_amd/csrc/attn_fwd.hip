@@ -21,74 +21,26 @@
 // LDS tile layout: [16-byte column chunk c][key] so that both the key-row reads for S^T and
 // the transposed value reads touch contiguous 256-byte spans.
 
-#include "common.hpp"
+#include "attn_common.hpp"
 #include "launch.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int kKeysPerTile = 32;
-constexpr int kFwdThreads = 256;  // 4 waves gather every tile; waves without heads only gather
-constexpr int kMaxTopK = 4096;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// Joins two transpose reads into one 8-slot bf16 MFMA operand (slots 0..3, then 4..7).
-__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
-  const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-// Compacts the valid slots of one selection row (0 <= idx < n_pools; -1 marks an empty
-// slot, and any other value is skipped the same way so that no gather leaves the table)
-// into sel[], in slot order, and returns their count.  All threads of the block call it.
-__device__ int compact_selection(const int32_t* __restrict__ irow, int k, int64_t n_pools,
-                                 int32_t* sel, int* wave_tmp) {
-  const int nthreads = kFwdThreads;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int nwaves = nthreads >> 6;
-  int base = 0;
-  for (int s0 = 0; s0 < k; s0 += nthreads) {
-    const int s = s0 + threadIdx.x;
-    const int32_t v = s < k ? irow[s] : -1;
-    const bool valid = v >= 0 && v < n_pools;
-    const uint64_t ballot = __ballot(valid);
-    const int before = __popcll(ballot & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tmp[wid] = __popcll(ballot);
-    __syncthreads();
-    int off = base;
-    int tot = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int c = wave_tmp[w];
-      if (w < wid) off += c;
-      tot += c;
-    }
-    if (valid) sel[off + before] = v;
-    base += tot;
-    __syncthreads();
-  }
-  return base;
-}
-
 template <int DQK, int DV, bool SEPARATE_V, bool OUT_F32>
-__global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(
+__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     void* __restrict__ o, float* __restrict__ lse, int64_t n_pools, int h,
     float scale_log2) {
-  constexpr int kChunksQK = DQK / 8;                       // 16-byte chunks of a key row
-  constexpr int kChunksV = SEPARATE_V ? DV / 8 : 0;        // chunks of a separate value row
-  constexpr int kChunksRow = kChunksQK + kChunksV;
-  constexpr int kKS = DQK / 32;                            // MFMA steps of q . k
-  constexpr int kNB = DV / 16;                             // 16-dim output blocks
-  constexpr int kTileChunks = kChunksRow * kKeysPerTile;
-  constexpr int kVBase = SEPARATE_V ? kChunksQK : 0;       // first chunk of V in a tile row
+  using Gather = TileGather<DQK, DV, SEPARATE_V>;
+  constexpr int kKS = DQK / 32;  // MFMA steps of q . k
+  constexpr int kNB = DV / 16;   // 16-dim output blocks
   static_assert(DQK % 32 == 0 && DV % 16 == 0, "tile shapes");
 
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileChunks * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[Gather::kTileBytes];
   __shared__ int32_t sel[kMaxTopK];
-  __shared__ int wave_tmp[kFwdThreads / 64];
+  __shared__ int wave_tmp[kAttnThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,43 +70,13 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(
   float l_run = 0.0f;
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-  // Gather assignment: thread -> one key of the tile (tid % 32), chunk columns tid/32 + 8i.
-  const int my_key = tid & (kKeysPerTile - 1);
-  constexpr int kColStep = kFwdThreads / kKeysPerTile;
-  constexpr int kChunksPerThread = (kTileChunks + kFwdThreads - 1) / kFwdThreads;
-  u32x4 pre[kChunksPerThread];
-
-  auto gather = [&](int t) {
-    const int slot = t * kKeysPerTile + my_key;
-    const int32_t p = slot < n_valid ? sel[slot] : -1;
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      u32x4 val = {0u, 0u, 0u, 0u};
-      const int c = (tid >> 5) + i * kColStep;
-      if (c < kChunksRow && p >= 0) {
-        const uint16_t* src = (!SEPARATE_V || c < kChunksQK)
-                                  ? kv + static_cast<int64_t>(p) * ld_kv + c * 8
-                                  : v + static_cast<int64_t>(p) * ld_v + (c - kChunksQK) * 8;
-        val = *reinterpret_cast<const u32x4*>(src);
-      }
-      pre[i] = val;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = (tid >> 5) + i * kColStep;
-      if (c < kChunksRow)
-        *reinterpret_cast<u32x4*>(&tile[(c * kKeysPerTile + my_key) * 16]) = pre[i];
-    }
-  };
-
-  if (n_tiles > 0) gather(0);
+  Gather gather;
+  if (n_tiles > 0) gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
   for (int t = 0; t < n_tiles; ++t) {
     __syncthreads();  // previous tile fully consumed
-    store();
+    gather.store(tile);
     __syncthreads();
-    if (t + 1 < n_tiles) gather(t + 1);
+    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
     if (!wave_has_heads) continue;
 
     // S^T = K . Q^T for the 32 keys of the tile (two 16-key row blocks).
@@ -163,8 +85,8 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(
     for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &tile[((4 * ks + g) * kKeysPerTile + mb * 16 + r16) * 16]);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]);
         s[mb] = mfma16x16x32_bf16(a, qf[ks], s[mb]);
       }
     }
@@ -205,18 +127,10 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) oacc[nb] *= alpha;
 
-    // O^T += V^T . P^T.  Contraction slots 0..3 <-> keys 4g+e, 4..7 <-> keys 16+4g+e,
-    // matching where the S^T accumulator left the probabilities.
-    const int tr_key = 4 * g + (r16 >> 2);
-    const int tr_col = 4 * (r16 & 3);  // dims within a 16-dim block
+    // O^T += V^T . P^T, contraction over the tile's keys in the S^T slot order.
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const int dim = nb * 16 + tr_col;
-      const int c = kVBase + (dim >> 3);
-      const int byte = (dim & 7) * 2;
-      const i16x4 lo = lds_read_tr16(&tile[(c * kKeysPerTile + tr_key) * 16 + byte]);
-      const i16x4 hi = lds_read_tr16(&tile[(c * kKeysPerTile + 16 + tr_key) * 16 + byte]);
-      const bf16x8 vt = join_tr(lo, hi);
+      const bf16x8 vt = tile_cols_transposed(tile, Gather::kVBase, nb, g, r16);
       oacc[nb] = mfma16x16x32_bf16(vt, pf_hi, oacc[nb]);
       oacc[nb] = mfma16x16x32_bf16(vt, pf_lo, oacc[nb]);
     }
@@ -243,7 +157,8 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(
     }
   }
   if (g == 0)
-    lse[row * h + head] = n_valid > 0 ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+    lse[row * h + head] =
+        n_valid > 0 ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
 template <int DQK, int DV, bool SEP, bool F32>
@@ -252,7 +167,7 @@ hipError_t launch_fwd_variant(const void* q, const void* kv, int64_t ld_kv, cons
                               int64_t nq, int64_t n_pools, int h, float scale,
                               hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, SEP, F32>), dim3(static_cast<unsigned>(nq)),
-                     dim3(kFwdThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
                      ld_v, idx, k, o, lse, n_pools, h, scale * kLog2e);
   return hipGetLastError();
