@@ -81,20 +81,25 @@ __device__ __forceinline__ void tile_grads(const uint8_t* tile, const bf16x8* qf
   constexpr int kVS = DV / 32;
   f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // With V aliased to the key row's first DV columns, one LDS read feeds both products.
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-      s[mb] = mfma16x16x32_bf16(
-          *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]), qf[ks],
-          s[mb]);
+    for (int mb = 0; mb < 2; ++mb) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]);
+      s[mb] = mfma16x16x32_bf16(a, qf[ks], s[mb]);
+      if (VBASE == 0 && ks < kVS) dp[mb] = mfma16x16x32_bf16(a, dof[ks], dp[mb]);
+    }
+  if constexpr (VBASE != 0) {
 #pragma unroll
-  for (int ks = 0; ks < kVS; ++ks)
+    for (int ks = 0; ks < kVS; ++ks)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-      dp[mb] = mfma16x16x32_bf16(
-          *reinterpret_cast<const bf16x8*>(&tile[tile_off(VBASE + 4 * ks + g, mb * 16 + r16)]),
-          dof[ks], dp[mb]);
+      for (int mb = 0; mb < 2; ++mb)
+        dp[mb] = mfma16x16x32_bf16(
+            *reinterpret_cast<const bf16x8*>(&tile[tile_off(VBASE + 4 * ks + g, mb * 16 + r16)]),
+            dof[ks], dp[mb]);
+  }
   i16x8 ph, pl, sh, sl;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -142,9 +147,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
     const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
     const float* __restrict__ delta, float* __restrict__ dq, int64_t n_pools, int h,
     float scale_log2, float scale) {
-  using Gather = TileGather<DQK, DV, SEPARATE_V>;
+  constexpr int kTileBytes = TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes;
+  using Dma = TileDma<DQK, DV, SEPARATE_V, pick_depth(kTileBytes, kMaxTopK * 4 + 64)>;
   constexpr int kNQ = DQK / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[Gather::kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
   __shared__ int32_t sel[kMaxTopK];
   __shared__ int wave_tmp[kAttnThreads / 64];
 
@@ -162,23 +168,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
   load_head_operands<DQK, DV>(q, d_o, row, h, head, head_ok, g, qf, dof);
   const float lse2 = head_ok && n_valid > 0 ? lse[row * h + head] * kLog2e : 0.0f;
   const float dh = head_ok ? delta[row * h + head] : 0.0f;
+  DSA_WAIT_VMCNT(0);  // operands in registers before the tile pipeline starts
 
   f32x4 acc[kNQ];
 #pragma unroll
   for (int nb = 0; nb < kNQ; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-  Gather gather;
-  if (n_tiles > 0) gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
-    gather.store(tile);
-    __syncthreads();
-    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
-    if (!wave_has_heads) continue;
+  Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                     [&](const uint8_t* tile, int t) {
+    if (!wave_has_heads) return;
     TileGrads tg;
-    tile_grads<DQK, DV, Gather::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
-                                        scale_log2, lse2, dh, g, r16, tg);
+    tile_grads<DQK, DV, Dma::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
+                                     scale_log2, lse2, dh, g, r16, tg);
     // dQ^T += K^T . dS^T over the tile's keys.
 #pragma unroll
     for (int nb = 0; nb < kNQ; ++nb) {
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
       acc[nb] = mfma16x16x32_bf16(kt, tg.ds_hi, acc[nb]);
       acc[nb] = mfma16x16x32_bf16(kt, tg.ds_lo, acc[nb]);
     }
-  }
+  });
   if (!head_ok) return;
   float* out = dq + (row * h + head) * DQK;
 #pragma unroll
@@ -200,11 +202,17 @@ constexpr int kPsRow = kHeadsPad + 8;  // bf16 per key row of the P / dS arrays 
 
 template <int DQK, int DV, bool SEPARATE_V>
 struct DkvLds {
-  using Gather = TileGather<DQK, DV, SEPARATE_V>;
   static constexpr int kStageQ = kHeadsPad * (DQK + 8) * 2;
   static constexpr int kStageO = kHeadsPad * (DV + 8) * 2;
-  static constexpr int kShared0 = kStageQ > kStageO ? kStageQ : kStageO;
-  static constexpr int kShared = kShared0 > Gather::kTileBytes ? kShared0 : Gather::kTileBytes;
+  static constexpr int kStage = kStageQ > kStageO ? kStageQ : kStageO;
+  static constexpr int kOther = 4 * kKeysPerTile * kPsRow * 2 + kMaxTopK * 4 + 64;
+  static constexpr int kTileBytes = TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes;
+  // Tile stages share the staging region; deepest pipeline that fits beside the rest.
+  static constexpr int kDepth = 3 * kTileBytes + kOther <= 160 * 1024 - 256   ? 3
+                                : 2 * kTileBytes + kOther <= 160 * 1024 - 256 ? 2
+                                                                              : 1;
+  using Dma = TileDma<DQK, DV, SEPARATE_V, kDepth>;
+  static constexpr int kShared = kStage > Dma::kLdsBytes ? kStage : Dma::kLdsBytes;
 };
 
 // B operand for a product contracting over heads: lane (g, r) gets X[32 ks + 8 g + s][col0 + r]
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
     const float* __restrict__ delta, float* __restrict__ dkv, float* __restrict__ dv,
     int64_t n_pools, int h, float scale_log2, float scale) {
   using Lds = DkvLds<DQK, DV, SEPARATE_V>;
-  using Gather = typename Lds::Gather;
+  using Dma = typename Lds::Dma;
   constexpr int kCols = DQK / 4;     // output columns owned by each wave
   constexpr int kNBW = kCols / 16;
   static_assert(kCols % 16 == 0, "column split");
@@ -234,7 +242,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ps[4][kKeysPerTile * kPsRow];
   __shared__ int32_t sel[kMaxTopK];
   __shared__ int wave_tmp[kAttnThreads / 64];
-  uint8_t* tile = shared;
   uint16_t* stage = reinterpret_cast<uint16_t*>(shared);
 
   const int tid = threadIdx.x;
@@ -292,20 +299,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   const float lse2 = head_ok ? lse[row * h + head] * kLog2e : 0.0f;
   const float dh = head_ok ? delta[row * h + head] : 0.0f;
   const bool fold_v = dv == nullptr;  // V aliased and its gradient folded into dkv
+  DSA_WAIT_VMCNT(0);  // operands in registers before the tile pipeline starts
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-  Gather gather;
-  gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();  // staging reads / previous tile and P, dS arrays fully consumed
-    gather.store(tile);
-    __syncthreads();
-    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
+  __syncthreads();  // the staging copies are fully read before tiles overwrite them
+  Dma::for_each_tile(shared, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                     [&](const uint8_t* tile, int t) {
     const int slot0 = t * kKeysPerTile;
     TileGrads tg;
     if (wave_has_heads) {
-      tile_grads<DQK, DV, Gather::kVBase>(tile, qf, dof, slot0, n_valid, head_ok, scale_log2,
-                                          lse2, dh, g, r16, tg);
+      tile_grads<DQK, DV, Dma::kVBase>(tile, qf, dof, slot0, n_valid, head_ok, scale_log2,
+                                       lse2, dh, g, r16, tg);
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -325,7 +329,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
         ps[2][at] = shb;
         ps[3][at] = float_to_bf16_bits(d - bf16_bits_to_float(shb));
       }
-    __syncthreads();
+    DSA_WAIT_LGKMCNT0();
+    tile_barrier();
     // This wave's columns of dK_tile = dS^T . Q and dV_tile = P^T . dO (64-head contraction).
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
         }
       }
     }
-  }
+  });
 }
 
 template <int DQK, int DV, bool SEP>

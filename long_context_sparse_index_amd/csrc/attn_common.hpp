@@ -50,49 +50,128 @@ __device__ inline int compact_selection(const int32_t* __restrict__ irow, int k,
   return base;
 }
 
-// Gather of one tile of 32 selected rows into LDS, laid out [16-byte chunk c][key]: chunks
-// [0, DQK/8) are the key row, then (separate V only) DV/8 chunks of the value row.  Thread t
-// loads key t % 32, chunk columns t / 32 + 8 i, into registers (load), then writes them to
-// LDS (store), so the next tile's loads can be in flight while the current one is used.
-template <int DQK, int DV, bool SEPARATE_V>
-struct TileGather {
+// Waits until at most `n` vector-memory operations of this wave are outstanding (n < 64).
+#define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
+// Waits until this wave's LDS operations (ds_read / ds_write) have completed.
+#define DSA_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Deepest tile pipeline (<= 3 stages) whose LDS fits next to `other_bytes` of LDS.
+constexpr int pick_depth(int tile_bytes, int other_bytes) {
+  return 3 * tile_bytes + other_bytes <= 160 * 1024 - 256   ? 3
+         : 2 * tile_bytes + other_bytes <= 160 * 1024 - 256 ? 2
+                                                            : 1;
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations but does not
+// wait for outstanding vector-memory operations (the tile pipeline below waits for exactly
+// the loads it needs with DSA_WAIT_VMCNT).  LDS writes made with ds_write must be waited
+// for (lgkmcnt) by the caller before it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One asynchronous 16-byte-per-lane global -> LDS load: lane l's 16 bytes at `src` land at
+// LDS byte address lds_addr + 16 l (lds_addr wave-uniform).  Written as inline assembly so
+// that the compiler's wait insertion does not treat it as an LDS store and drain every
+// outstanding load before the next LDS read; the tile pipeline below waits for exactly
+// the loads it needs (the compiler's own waits only count more operations, never fewer).
+__device__ __forceinline__ void dma_16b(const void* src, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(static_cast<const char*>(p))));
+}
+
+// Asynchronous gather of tiles of 32 selected rows straight into LDS (global_load_lds,
+// 16 bytes per lane), `DEPTH` tiles deep.  A tile is laid out [16-byte chunk c][key]:
+// chunks [0, DQK/8) are the key row, then (separate V only) DV/8 chunks of the value row.
+// One load instruction fills 1 KB of LDS (64 lanes x 16 bytes) = chunk columns 2j, 2j+1 of
+// all 32 keys; the tile's instructions are split evenly over the 4 waves.  Keys past the
+// last valid slot repeat the last valid row (their probabilities are masked to zero).
+template <int DQK, int DV, bool SEPARATE_V, int DEPTH>
+struct TileDma {
   static constexpr int kChunksQK = DQK / 8;
   static constexpr int kChunksRow = kChunksQK + (SEPARATE_V ? DV / 8 : 0);
-  static constexpr int kTileChunks = kChunksRow * kKeysPerTile;
-  static constexpr int kTileBytes = kTileChunks * 16;
+  static constexpr int kTileBytes = kChunksRow * kKeysPerTile * 16;
   static constexpr int kVBase = SEPARATE_V ? kChunksQK : 0;  // first chunk of V in a row
-  static constexpr int kColStep = kAttnThreads / kKeysPerTile;
-  static constexpr int kPerThread = (kTileChunks + kAttnThreads - 1) / kAttnThreads;
-  u32x4 pre[kPerThread];
+  static constexpr int kInstr = kChunksRow / 2;
+  static constexpr int kPerWave = kInstr / (kAttnThreads / 64);
+  static constexpr int kLdsBytes = DEPTH * kTileBytes;
+  static_assert(kChunksRow % 2 == 0 && kInstr % (kAttnThreads / 64) == 0, "tile split");
+  static_assert(DEPTH >= 1 && DEPTH <= 3 && kPerWave * (DEPTH - 1) < 64, "vmcnt range");
 
-  __device__ __forceinline__ void load(int t, const int32_t* sel, int n_valid,
-                                       const uint16_t* __restrict__ kv, int64_t ld_kv,
-                                       const uint16_t* __restrict__ v, int64_t ld_v) {
-    const int tid = threadIdx.x;
-    const int slot = t * kKeysPerTile + (tid & (kKeysPerTile - 1));
-    const int32_t p = slot < n_valid ? sel[slot] : -1;
+  // Issues the loads of tile t into stage `stage` of `tiles`.
+  __device__ __forceinline__ static void issue(uint8_t* tiles, int stage, int t,
+                                               const int32_t* sel, int n_valid,
+                                               const uint16_t* __restrict__ kv, int64_t ld_kv,
+                                               const uint16_t* __restrict__ v, int64_t ld_v) {
+    const int lane = threadIdx.x & 63;
+    // Wave-uniform: keeps the LDS destinations (M0) in scalar registers.
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int slot = t * kKeysPerTile + (lane & (kKeysPerTile - 1));
+    slot = slot < n_valid ? slot : n_valid - 1;
+    const int64_t p = sel[slot];
+    const uint32_t base = lds_address(tiles) + stage * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      u32x4 val = {0u, 0u, 0u, 0u};
-      const int c = (tid >> 5) + i * kColStep;
-      if (c < kChunksRow && p >= 0) {
-        const uint16_t* src = (!SEPARATE_V || c < kChunksQK)
-                                  ? kv + static_cast<int64_t>(p) * ld_kv + c * 8
-                                  : v + static_cast<int64_t>(p) * ld_v + (c - kChunksQK) * 8;
-        val = *reinterpret_cast<const u32x4*>(src);
-      }
-      pre[i] = val;
+    for (int i = 0; i < kPerWave; ++i) {
+      const int j = wid * kPerWave + i;
+      const int c = 2 * j + (lane >> 5);
+      const uint16_t* src = (!SEPARATE_V || c < kChunksQK) ? kv + p * ld_kv + c * 8
+                                                           : v + p * ld_v + (c - kChunksQK) * 8;
+      dma_16b(src, base + j * 1024);
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* tile) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = (tid >> 5) + i * kColStep;
-      if (c < kChunksRow)
-        *reinterpret_cast<u32x4*>(&tile[(c * kKeysPerTile + (tid & (kKeysPerTile - 1))) * 16]) =
-            pre[i];
+  // Waits for this wave's loads of a tile when `younger` later tiles may stay in flight.
+  __device__ __forceinline__ static void wait(int younger) {
+    if (younger <= 0) {
+      DSA_WAIT_VMCNT(0);
+    } else if (younger == 1) {
+      DSA_WAIT_VMCNT(kPerWave);
+    } else {
+      DSA_WAIT_VMCNT(2 * kPerWave);
+    }
+  }
+
+  // Runs body(tile_bytes, t) for every tile t in order with DEPTH - 1 tiles prefetched.
+  // All threads of the block must call it (it contains barriers).
+  template <class Body>
+  __device__ __forceinline__ static void for_each_tile(uint8_t* tiles, int n_tiles,
+                                                       const int32_t* sel, int n_valid,
+                                                       const uint16_t* __restrict__ kv,
+                                                       int64_t ld_kv,
+                                                       const uint16_t* __restrict__ v,
+                                                       int64_t ld_v, Body&& body) {
+    if constexpr (DEPTH == 1) {
+      for (int t = 0; t < n_tiles; ++t) {
+        tile_barrier();  // the previous tile is consumed
+        issue(tiles, 0, t, sel, n_valid, kv, ld_kv, v, ld_v);
+        DSA_WAIT_VMCNT(0);
+        tile_barrier();
+        body(static_cast<const uint8_t*>(tiles), t);
+      }
+    } else {
+      for (int s = 0; s < DEPTH - 1 && s < n_tiles; ++s)
+        issue(tiles, s, s, sel, n_valid, kv, ld_kv, v, ld_v);
+      for (int t = 0; t < n_tiles; ++t) {
+        const int ahead = n_tiles - 1 - t;
+        wait(ahead < DEPTH - 2 ? ahead : DEPTH - 2);
+        tile_barrier();  // tile t is in LDS for every wave; tile t-1 is consumed
+        if (t + DEPTH - 1 < n_tiles)
+          issue(tiles, (t + DEPTH - 1) % DEPTH, t + DEPTH - 1, sel, n_valid, kv, ld_kv, v,
+                ld_v);
+        body(static_cast<const uint8_t*>(tiles + (t % DEPTH) * kTileBytes), t);
+      }
     }
   }
 };

@@ -16,7 +16,9 @@
 // accumulator already in the B-operand layout of the P.V product.  V^T is read from the
 // same row-major LDS tile with the LDS transpose read, so V costs no second gather or copy.
 // The selection row is first compacted in LDS (valid slots in slot order), so tiles of
-// empty (-1) slots are never visited; only the last tile can be partial.
+// empty (-1) slots are never visited; only the last tile can be partial.  Tiles are
+// gathered with asynchronous global->LDS loads, up to three tiles deep, so the gather of
+// the next tiles overlaps the MFMA work on the current one without staging registers.
 //
 // LDS tile layout: [16-byte column chunk c][key] so that both the key-row reads for S^T and
 // the transposed value reads touch contiguous 256-byte spans.
@@ -33,12 +35,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     void* __restrict__ o, float* __restrict__ lse, int64_t n_pools, int h,
     float scale_log2) {
-  using Gather = TileGather<DQK, DV, SEPARATE_V>;
+  constexpr int kTileBytes = TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes;
+  using Dma = TileDma<DQK, DV, SEPARATE_V, pick_depth(kTileBytes, kMaxTopK * 4 + 64)>;
   constexpr int kKS = DQK / 32;  // MFMA steps of q . k
   constexpr int kNB = DV / 16;   // 16-dim output blocks
   static_assert(DQK % 32 == 0 && DV % 16 == 0, "tile shapes");
 
-  __shared__ __attribute__((aligned(16))) uint8_t tile[Gather::kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
   __shared__ int32_t sel[kMaxTopK];
   __shared__ int wave_tmp[kAttnThreads / 64];
 
@@ -62,6 +65,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     for (int ks = 0; ks < kKS; ++ks)
       qf[ks] = head_ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32) : bf16x8_zero();
   }
+  // Land the operand loads before the tile pipeline starts: the pipeline's own waits count
+  // only its tile loads, and an operand load still pending inside the loop would make the
+  // compiler wait for every outstanding load there.
+  DSA_WAIT_VMCNT(0);
 
   f32x4 oacc[kNB];
 #pragma unroll
@@ -70,14 +77,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
   float l_run = 0.0f;
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-  Gather gather;
-  if (n_tiles > 0) gather.load(0, sel, n_valid, kv, ld_kv, v, ld_v);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();  // previous tile fully consumed
-    gather.store(tile);
-    __syncthreads();
-    if (t + 1 < n_tiles) gather.load(t + 1, sel, n_valid, kv, ld_kv, v, ld_v);
-    if (!wave_has_heads) continue;
+  Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                     [&](const uint8_t* tile, int t) {
+    if (!wave_has_heads) return;
 
     // S^T = K . Q^T for the 32 keys of the tile (two 16-key row blocks).
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -130,11 +132,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     // O^T += V^T . P^T, contraction over the tile's keys in the S^T slot order.
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const bf16x8 vt = tile_cols_transposed(tile, Gather::kVBase, nb, g, r16);
+      const bf16x8 vt = tile_cols_transposed(tile, Dma::kVBase, nb, g, r16);
       oacc[nb] = mfma16x16x32_bf16(vt, pf_hi, oacc[nb]);
       oacc[nb] = mfma16x16x32_bf16(vt, pf_lo, oacc[nb]);
     }
-  }
+  });
 
   // Finish: combine the four lane groups' partial sums of each head.
   float l_tot = l_run + shfl_xor(l_run, 16);

@@ -70,8 +70,9 @@ def test_backward_latent_576_random_selection(gpu, h):
     assert_close(dq.cpu().numpy(), rq, "dQ")
     assert_close(dkv.cpu().numpy(), rk, "dKV")
     assert np.all(dq[0].cpu().numpy() == 0.0)  # no valid slot: nothing to differentiate
-    # one valid slot: the softmax is constant, so dQ vanishes up to fp32 rounding of P and D
-    assert np.abs(dq[1].cpu().numpy()).max() <= 1e-5 * float(np.sqrt(np.mean(rq * rq)))
+    # one valid slot: the softmax is constant, so dQ vanishes up to the fp32 rounding gap
+    # between dP (MFMA summation order) and D = dO . O (|dP| ~ 20 here)
+    assert np.abs(dq[1].cpu().numpy()).max() <= 1e-4 * float(np.sqrt(np.mean(rq * rq)))
 
 
 def test_backward_64k_full_size(gpu):
