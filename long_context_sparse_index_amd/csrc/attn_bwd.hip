@@ -73,7 +73,7 @@ struct TileGrads {
 };
 
 template <int DQK, int DV, int VBASE>
-__device__ __forceinline__ void tile_grads(const uint8_t* tile, const bf16x8* qf,
+__device__ __forceinline__ void tile_grads(lds_ptr tile, const bf16x8* qf,
                                            const bf16x8* dof, int slot0, int n_valid,
                                            bool head_ok, float scale_log2, float lse2,
                                            float dh, int g, int r16, TileGrads& out) {
@@ -86,8 +86,7 @@ __device__ __forceinline__ void tile_grads(const uint8_t* tile, const bf16x8* qf
   for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]);
+      const bf16x8 a = lds_load_bf16x8(tile + tile_off(4 * ks + g, mb * 16 + r16));
       s[mb] = mfma16x16x32_bf16(a, qf[ks], s[mb]);
       if (VBASE == 0 && ks < kVS) dp[mb] = mfma16x16x32_bf16(a, dof[ks], dp[mb]);
     }
@@ -97,8 +96,8 @@ __device__ __forceinline__ void tile_grads(const uint8_t* tile, const bf16x8* qf
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         dp[mb] = mfma16x16x32_bf16(
-            *reinterpret_cast<const bf16x8*>(&tile[tile_off(VBASE + 4 * ks + g, mb * 16 + r16)]),
-            dof[ks], dp[mb]);
+            lds_load_bf16x8(tile + tile_off(VBASE + 4 * ks + g, mb * 16 + r16)), dof[ks],
+            dp[mb]);
   }
   i16x8 ph, pl, sh, sl;
 #pragma unroll
@@ -176,15 +175,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
   Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
-                     [&](const uint8_t* tile, int t) {
+                     [&](lds_ptr tile, int t) {
     if (!wave_has_heads) return;
     TileGrads tg;
     tile_grads<DQK, DV, Dma::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
                                      scale_log2, lse2, dh, g, r16, tg);
     // dQ^T += K^T . dS^T over the tile's keys.
+    const lds_ptr kt_base = tile + tile_tr_lane_off(0, g, r16);
 #pragma unroll
     for (int nb = 0; nb < kNQ; ++nb) {
-      const bf16x8 kt = tile_cols_transposed(tile, 0, nb, g, r16);
+      const bf16x8 kt = tile_tr_block(kt_base, nb);
       acc[nb] = mfma16x16x32_bf16(kt, tg.ds_hi, acc[nb]);
       acc[nb] = mfma16x16x32_bf16(kt, tg.ds_lo, acc[nb]);
     }
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
   __syncthreads();  // the staging copies are fully read before tiles overwrite them
   Dma::for_each_tile(shared, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
-                     [&](const uint8_t* tile, int t) {
+                     [&](lds_ptr tile, int t) {
     const int slot0 = t * kKeysPerTile;
     TileGrads tg;
     if (wave_has_heads) {

@@ -87,10 +87,6 @@ __device__ __forceinline__ void dma_16b(const void* src, uint32_t lds_addr) {
       : "memory", "m0");
 }
 
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const char*)(static_cast<const char*>(p))));
-}
 
 // Asynchronous gather of tiles of 32 selected rows straight into LDS (global_load_lds,
 // 16 bytes per lane), `DEPTH` tiles deep.  A tile is laid out [16-byte chunk c][key]:
@@ -121,7 +117,7 @@ struct TileDma {
     int slot = t * kKeysPerTile + (lane & (kKeysPerTile - 1));
     slot = slot < n_valid ? slot : n_valid - 1;
     const int64_t p = sel[slot];
-    const uint32_t base = lds_address(tiles) + stage * kTileBytes;
+    const uint32_t base = lds_addr_of(tiles) + stage * kTileBytes;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int j = wid * kPerWave + i;
@@ -143,7 +139,8 @@ struct TileDma {
     }
   }
 
-  // Runs body(tile_bytes, t) for every tile t in order with DEPTH - 1 tiles prefetched.
+  // Runs body(tile, t) for every tile t in order with DEPTH - 1 tiles prefetched; `tile` is
+  // an LDS pointer to the tile.
   // All threads of the block must call it (it contains barriers).
   template <class Body>
   __device__ __forceinline__ static void for_each_tile(uint8_t* tiles, int n_tiles,
@@ -158,7 +155,7 @@ struct TileDma {
         issue(tiles, 0, t, sel, n_valid, kv, ld_kv, v, ld_v);
         DSA_WAIT_VMCNT(0);
         tile_barrier();
-        body(static_cast<const uint8_t*>(tiles), t);
+        body(lds_ptr_of(tiles), t);
       }
     } else {
       for (int s = 0; s < DEPTH - 1 && s < n_tiles; ++s)
@@ -170,7 +167,7 @@ struct TileDma {
         if (t + DEPTH - 1 < n_tiles)
           issue(tiles, (t + DEPTH - 1) % DEPTH, t + DEPTH - 1, sel, n_valid, kv, ld_kv, v,
                 ld_v);
-        body(static_cast<const uint8_t*>(tiles + (t % DEPTH) * kTileBytes), t);
+        body(lds_ptr_of(tiles) + (t % DEPTH) * kTileBytes, t);
       }
     }
   }
@@ -179,18 +176,17 @@ struct TileDma {
 // Byte offset in a tile of the 16-byte chunk holding columns [8c, 8c + 8) of tile key `key`.
 __device__ __forceinline__ int tile_off(int c, int key) { return (c * kKeysPerTile + key) * 16; }
 
-// MFMA operand "X^T" for columns [16 nb, 16 nb + 16) of a tile, contraction over the tile's
-// 32 keys: lane (g, r) gets X[key][16 nb + r] for keys 4g + e (slots 0..3) and 16 + 4g + e
-// (slots 4..7), the slot order in which an S^T accumulator holds its probabilities.
-// `cbase` is the first chunk of X in a tile row.
-__device__ __forceinline__ bf16x8 tile_cols_transposed(const uint8_t* tile, int cbase, int nb,
-                                                       int g, int r16) {
+// Lane part of the LDS address of a transposed tile operand (see tile_tr_block):
+// the operand for column block nb is then at offset nb * 1024 (keys 4g + e) and
+// nb * 1024 + 256 (keys 16 + 4g + e), so one base address serves every block.
+__device__ __forceinline__ int tile_tr_lane_off(int cbase, int g, int r16) {
   const int key = 4 * g + (r16 >> 2);
-  const int col = nb * 16 + 4 * (r16 & 3);
-  const int c = cbase + (col >> 3);
-  const int byte = (col & 7) * 2;
-  const i16x4 lo = lds_read_tr16(&tile[tile_off(c, key) + byte]);
-  const i16x4 hi = lds_read_tr16(&tile[tile_off(c, 16 + key) + byte]);
+  return tile_off(cbase + ((r16 & 3) >> 1), key) + (r16 & 1) * 8;
+}
+
+__device__ __forceinline__ bf16x8 tile_tr_block(lds_ptr lane_base, int nb) {
+  const i16x4 lo = lds_read_tr16_at(lane_base + nb * 1024);
+  const i16x4 hi = lds_read_tr16_at(lane_base + nb * 1024 + 16 * 16);
   return join_tr(lo, hi);
 }
 

@@ -29,6 +29,10 @@
 namespace dsa {
 namespace {
 
+// Largest log2 excess of a logit over the softmax reference that the fp32/bf16 arithmetic
+// of the P.V product tolerates (probabilities up to 2^64, sums far below fp32 overflow).
+constexpr float kRefHeadroomLog2 = 64.0f;
+
 template <int DQK, int DV, bool SEPARATE_V, bool OUT_F32>
 __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
@@ -70,73 +74,88 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
   // compiler wait for every outstanding load there.
   DSA_WAIT_VMCNT(0);
 
+  // Softmax reference per head (log2 domain): the first tile's maximum.  O = sum p V / sum p
+  // does not depend on the reference, so no accumulator is ever rescaled in the loop; a
+  // logit more than 2^64 above the reference (fp32 headroom) raises `overflow` and the
+  // token is redone after an exact max pass.
   f32x4 oacc[kNB];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
+  float m_ref = -__builtin_inff();
   float l_run = 0.0f;
-
+  bool overflow = false;
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-  Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
-                     [&](const uint8_t* tile, int t) {
-    if (!wave_has_heads) return;
 
-    // S^T = K . Q^T for the 32 keys of the tile (two 16-key row blocks).
+  // S^T = K . Q^T for the 32 keys of a tile (two 16-key row blocks), in log2 units, with
+  // slots past the last valid one at -inf; also returns the tile max of the lane's head.
+  auto tile_logits = [&](lds_ptr tile, int t, f32x8& x) {
+    const lds_ptr k_base = tile + tile_off(g, r16);
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&tile[tile_off(4 * ks + g, mb * 16 + r16)]);
+        const bf16x8 a = lds_load_bf16x8(k_base + ks * 2048 + mb * 256);
         s[mb] = mfma16x16x32_bf16(a, qf[ks], s[mb]);
       }
     }
-    // Online softmax in the log2 domain; lane column = head, rows = keys 16mb + 4g + i.
     const int slot0 = t * kKeysPerTile;
-    float x[2][4];
     float mt = -__builtin_inff();
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = slot0 + mb * 16 + g * 4 + i < n_valid;
-        x[mb][i] = ok ? s[mb][i] * scale_log2 : -__builtin_inff();
-        mt = __builtin_fmaxf(mt, x[mb][i]);
+        x[mb * 4 + i] = ok ? s[mb][i] * scale_log2 : -__builtin_inff();
+        mt = __builtin_fmaxf(mt, x[mb * 4 + i]);
       }
     mt = __builtin_fmaxf(mt, shfl_xor(mt, 16));
-    mt = __builtin_fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = __builtin_fmaxf(m_run, mt);  // finite: every tile has a valid slot
-    const float alpha = __builtin_exp2f(m_run - m_new);
-    m_run = m_new;
-    // Each probability goes to the MFMA as a bf16 pair hi + lo (lo = the bf16 rounding of
-    // p - hi), so the P.V product sees p to about 16 significant bits instead of 8.
-    i16x8 hbits, lbits;
-    float psum = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_exp2f(x[mb][i] - m_new);
-        psum += p;
-        const uint16_t hb = float_to_bf16_bits(p);
-        hbits[mb * 4 + i] = static_cast<short>(hb);
-        lbits[mb * 4 + i] = static_cast<short>(float_to_bf16_bits(p - bf16_bits_to_float(hb)));
-      }
-    const bf16x8 pf_hi = bf16x8_from_bits(hbits);
-    const bf16x8 pf_lo = bf16x8_from_bits(lbits);
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) oacc[nb] *= alpha;
+    return __builtin_fmaxf(mt, shfl_xor(mt, 32));
+  };
 
-    // O^T += V^T . P^T, contraction over the tile's keys in the S^T slot order.
+  // One pass of P.V over all tiles against the reference m_ref (taken from tile 0 when
+  // `ref_from_first` is set).
+  auto pv_pass = [&](bool ref_from_first) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const bf16x8 vt = tile_cols_transposed(tile, Dma::kVBase, nb, g, r16);
-      oacc[nb] = mfma16x16x32_bf16(vt, pf_hi, oacc[nb]);
-      oacc[nb] = mfma16x16x32_bf16(vt, pf_lo, oacc[nb]);
-    }
-  });
+    for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.0f;
+    Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                       [&](lds_ptr tile, int t) {
+      if (!wave_has_heads) return;
+      f32x8 x;
+      const float mt = tile_logits(tile, t, x);
+      if (ref_from_first && t == 0) m_ref = mt;
+      overflow |= mt > m_ref + kRefHeadroomLog2;
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_exp2f(x[e] - m_ref);
+      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // Each probability goes to the MFMA as a bf16 pair hi + lo, so the P.V product sees
+      // p to about 16 significant bits instead of 8.
+      bf16x8 pf_hi, pf_lo;
+      split_bf16x8(p, pf_hi, pf_lo);
+      // O^T += V^T . P^T, contraction over the tile's keys in the S^T slot order.
+      const lds_ptr vt_base = tile + tile_tr_lane_off(Dma::kVBase, g, r16);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const bf16x8 vt = tile_tr_block(vt_base, nb);
+        oacc[nb] = mfma16x16x32_bf16(vt, pf_hi, oacc[nb]);
+        oacc[nb] = mfma16x16x32_bf16(vt, pf_lo, oacc[nb]);
+      }
+    });
+  };
+
+  pv_pass(true);
+  if (__syncthreads_or(overflow)) {
+    // Rare: some logit far above the first tile's maximum.  Take the exact maximum first.
+    m_ref = -__builtin_inff();
+    Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                       [&](lds_ptr tile, int t) {
+      if (!wave_has_heads) return;
+      f32x8 x;
+      m_ref = __builtin_fmaxf(m_ref, tile_logits(tile, t, x));
+    });
+    pv_pass(false);
+  }
+  const float m_run = m_ref;
 
   // Finish: combine the four lane groups' partial sums of each head.
   float l_tot = l_run + shfl_xor(l_run, 16);

@@ -39,6 +39,29 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)p));
 }
 
+// LDS access through address-space-3 pointers: in-bounds pointer arithmetic lets a base
+// register plus a constant fold into the instruction's offset field (plain 32-bit integer
+// addresses may wrap, so the compiler would add every constant in a register instead).
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const lds_char* lds_ptr;
+
+__device__ __forceinline__ lds_ptr lds_ptr_of(const void* p) {
+  return (lds_ptr)(static_cast<const char*>(p));
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr_of(p)));
+}
+
+__device__ __forceinline__ bf16x8 lds_load_bf16x8(lds_ptr p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16_at(lds_ptr p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
 __device__ __forceinline__ int64_t visible_pools(int64_t t, int64_t n_pools) {
   const int64_t v = (t + 1) >> 2;
   return v < n_pools ? (v < 0 ? 0 : v) : n_pools;
@@ -53,6 +76,17 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Splits eight fp32 values into bf16 operands hi + lo (hi = RNE(x), lo = RNE(x - hi)), so
+// an MFMA over hi and lo sees x to about 16 significant bits.  Uses the hardware packed
+// bf16 conversion.
+__device__ __forceinline__ void split_bf16x8(f32x8 x, bf16x8& hi, bf16x8& lo) {
+  hi = __builtin_convertvector(x, bf16x8);
+  const f32x8 back = __builtin_convertvector(hi, f32x8);
+  lo = __builtin_convertvector(x - back, bf16x8);
 }
 
 // Whole-vector reinterpretations between bf16 operands and their 16-bit patterns.

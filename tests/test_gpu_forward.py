@@ -205,6 +205,31 @@ def test_attention_latent_576_random_selection(gpu, h):
     assert np.max(np.abs(lse_h[fin] - rl[fin])) < 1e-4
 
 
+def test_attention_logit_far_above_first_tile(gpu):
+    """The forward takes each head's softmax reference from the first gathered tile; a
+    later logit more than 2^64 above it must trigger the exact-maximum redo of the token."""
+    say("case: attention 576/512, huge logit in a later tile")
+    nq, h, p, k = 4, 64, 512, 256
+    g = torch.Generator(device=gpu).manual_seed(5)
+    q = torch.zeros((nq, h, 576), dtype=torch.bfloat16, device=gpu)
+    q[:, :, 0] = 64.0
+    q[:, :, 1:] = (0.01 * torch.randn((nq, h, 575), generator=g, device=gpu)).to(torch.bfloat16)
+    kv = (0.01 * torch.randn((p, 576), generator=g, device=gpu)).to(torch.bfloat16)
+    kv[300, 0] = 64.0    # logit ~ 4096/24: far above the first tile's (~0)
+    kv[301, 0] = -64.0
+    idx = torch.arange(k, dtype=torch.int32, device=gpu).repeat(nq, 1).contiguous()
+    idx[0, 100] = 300    # row 0: the huge key sits in tile 3
+    idx[1, 5] = 300      # row 1: the huge key is in the first tile (no redo)
+    idx[3, 200] = 301    # row 3: a huge negative logit only
+    scale = 1.0 / 24.0
+    o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=scale, d_v=512)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(q, kv, idx, scale, 512)
+    assert_close(o.cpu().numpy(), ro, "O")
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3 * np.max(np.abs(rl))
+    assert np.allclose(o[0].cpu().numpy(), kv[300, :512].float().cpu().numpy(), atol=1e-6)
+
+
 def test_chunked_matches_separate_calls_and_is_chunk_invariant(gpu):
     say("case: forward_chunked tiny_4k, chunks 4096/1000/7")
     q_i, k_i, w = I.index_inputs(TINY, gpu)
