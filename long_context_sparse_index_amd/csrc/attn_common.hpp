@@ -79,12 +79,9 @@ __device__ __forceinline__ void tile_barrier() {
 // outstanding load before the next LDS read; the tile pipeline below waits for exactly
 // the loads it needs (the compiler's own waits only count more operations, never fewer).
 __device__ __forceinline__ void dma_16b(const void* src, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds_addr)
-      : "memory", "m0");
+  // m0 (the LDS base of the load) is an input operand, so the compiler sets it and knows
+  // it is in use.
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
 }
 
 

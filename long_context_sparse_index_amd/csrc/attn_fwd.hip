@@ -87,15 +87,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
   // S^T = K . Q^T for the 32 keys of a tile (two 16-key row blocks), in log2 units, with
   // slots past the last valid one at -inf; also returns the tile max of the lane's head.
   auto tile_logits = [&](lds_ptr tile, int t, f32x8& x) {
-    const lds_ptr k_base = tile + tile_off(g, r16);
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // Key rows 16 mb + r of chunk column 4 ks + g.  Four independent accumulation chains
+    // (row block x parity of ks) keep back-to-back MFMAs free of dependences.
+    const lds_ptr k_base0 = tile + tile_off(g, r16);
+    const lds_ptr k_base1 = tile + tile_off(g, 16 + r16);
+    f32x4 s[2][2] = {};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = lds_load_bf16x8(k_base + ks * 2048 + mb * 256);
-        s[mb] = mfma16x16x32_bf16(a, qf[ks], s[mb]);
-      }
+      s[0][ks & 1] = mfma16x16x32_bf16(lds_load_bf16x8(k_base0 + ks * 2048), qf[ks], s[0][ks & 1]);
+      s[1][ks & 1] = mfma16x16x32_bf16(lds_load_bf16x8(k_base1 + ks * 2048), qf[ks], s[1][ks & 1]);
     }
     const int slot0 = t * kKeysPerTile;
     float mt = -__builtin_inff();
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = slot0 + mb * 16 + g * 4 + i < n_valid;
-        x[mb * 4 + i] = ok ? s[mb][i] * scale_log2 : -__builtin_inff();
+        x[mb * 4 + i] = ok ? (s[mb][0][i] + s[mb][1][i]) * scale_log2 : -__builtin_inff();
         mt = __builtin_fmaxf(mt, x[mb * 4 + i]);
       }
     mt = __builtin_fmaxf(mt, shfl_xor(mt, 16));
