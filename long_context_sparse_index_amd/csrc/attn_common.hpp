@@ -115,13 +115,21 @@ struct TileDma {
     slot = slot < n_valid ? slot : n_valid - 1;
     const int64_t p = sel[slot];
     const uint32_t base = lds_addr_of(tiles) + stage * kTileBytes;
+    if constexpr (!SEPARATE_V) {
+      // One row pointer; the wave's loads are at constant column offsets from it.
+      const uint16_t* rowp = kv + p * ld_kv + (2 * wid * kPerWave + (lane >> 5)) * 8;
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int j = wid * kPerWave + i;
-      const int c = 2 * j + (lane >> 5);
-      const uint16_t* src = (!SEPARATE_V || c < kChunksQK) ? kv + p * ld_kv + c * 8
-                                                           : v + p * ld_v + (c - kChunksQK) * 8;
-      dma_16b(src, base + j * 1024);
+      for (int i = 0; i < kPerWave; ++i)
+        dma_16b(rowp + i * 16, base + (wid * kPerWave + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int j = wid * kPerWave + i;
+        const int c = 2 * j + (lane >> 5);
+        const uint16_t* src =
+            c < kChunksQK ? kv + p * ld_kv + c * 8 : v + p * ld_v + (c - kChunksQK) * 8;
+        dma_16b(src, base + j * 1024);
+      }
     }
   }
 

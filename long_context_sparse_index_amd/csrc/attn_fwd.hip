@@ -23,6 +23,8 @@
 // LDS tile layout: [16-byte column chunk c][key] so that both the key-row reads for S^T and
 // the transposed value reads touch contiguous 256-byte spans.
 
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -182,15 +184,357 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
         n_valid > 0 ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
+// ---------------------------------------------------------------------------------------
+// Head-pair kernel, used wherever three tiles fit in LDS next to its exchange buffers.
+//
+// The kernel above makes every wave read the whole tile (its keys for S^T, its values for
+// O^T) for 16 heads and run the softmax of 16 heads x 32 keys per tile.  Here wave
+// w = (head half hh = w / 2, half kh = w % 2) serves 32 heads (two 16-head groups):
+//   * it computes the logits of both head groups for the 16 keys 16 kh .. 16 kh + 15 of
+//     each tile (full contraction; one key fragment read feeds both head groups) and their
+//     probabilities.  In the B-operand layout of the P.V product those 16 keys are exactly
+//     slots 4 kh .. 4 kh + 3 of every lane, so the two waves of a pair each write their
+//     half of the 16-byte operand into one shared LDS slot per lane and read back the
+//     whole operand after the tile barrier;
+//   * it accumulates O^T of the 32 heads over value-column half kh, so each transpose
+//     read of V feeds four MFMAs (two head groups x the hi/lo halves of P).
+// Per tile and block this halves the transpose reads and the key reads of the kernel
+// above, and no softmax work is done twice.  The pair shares one softmax reference per
+// head (the maximum of tile 0 over both key halves, exchanged once per pass) and adds its
+// two partial row sums at the end.  Loop body for tile t: logits and probabilities of
+// tile t + 1 and the whole P.V product of tile t (all independent, so the MFMA work of one
+// overlaps the vector work of the other), then one barrier, at which tile t is consumed,
+// the probabilities of tile t + 1 are exchanged and the tile two ahead has landed; the
+// load of the tile three ahead then reuses tile t's buffer.
+
+constexpr int kPairXchgBytes = 2 * 2 * 2 * 2 * 64 * 16;  // [buf][hh][hg][hi/lo][lane] x 16 B
+constexpr int kPairRedBytes = 4 * 64 * 8;                 // [wave][lane] x 2 floats
+
+template <int DQK, int DV, bool SEPARATE_V>
+constexpr bool pair_fits() {
+  return 3 * TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes + kPairXchgBytes + kPairRedBytes +
+             kMaxTopK * 4 + 64 <=
+         160 * 1024;
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+
+template <int DQK, int DV, bool SEPARATE_V, bool OUT_F32>
+__global__ __launch_bounds__(kAttnThreads) void attn_fwd_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
+    const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
+    void* __restrict__ o, float* __restrict__ lse, int64_t n_pools, int h,
+    float scale_log2) {
+  using Dma = TileDma<DQK, DV, SEPARATE_V, 3>;
+  constexpr int kKS = DQK / 32;   // q . k MFMA steps
+  constexpr int kNBH = DV / 32;   // 16-column output blocks per value half
+  static_assert(DQK % 64 == 0 && DV % 32 == 0, "tile shapes");
+  static_assert(pair_fits<DQK, DV, SEPARATE_V>(), "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pxchg[kPairXchgBytes];
+  __shared__ __attribute__((aligned(16))) f32x2 red[kPairRedBytes / 8];
+  __shared__ int32_t sel[kMaxTopK];
+  __shared__ int wave_tmp[kAttnThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = wid >> 1;
+  const int kh = wid & 1;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int64_t row = blockIdx.x;
+  const bool compute = hh * 32 < h;  // wave-uniform; waves without heads only gather
+
+  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
+  const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
+
+  // Queries of the two head groups as B operands (lane column = head).
+  bf16x8 qf[2][kKS];
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const int head = hh * 32 + hg * 16 + r16;
+    const bool ok = head < h;
+    const uint16_t* qrow = q + (row * h + (ok ? head : 0)) * DQK + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      qf[hg][ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32) : bf16x8_zero();
+  }
+  DSA_WAIT_VMCNT(0);  // the tile pipeline's waits count only tile loads
+
+  f32x4 oacc[2][kNBH];
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+    for (int nb = 0; nb < kNBH; ++nb) oacc[hg][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l_tot[2] = {0.f, 0.f};
+  bool overflow = false;
+
+  const uint32_t tiles_a = lds_addr_of(tiles);
+  // Key rows 16 kh + r of chunk column 4 ks + g for the logits; transposed value blocks of
+  // value half kh for O^T.
+  const int k_lane = tile_off(g, 16 * kh + r16);
+  const int v_lane = tile_tr_lane_off(Dma::kVBase, g, r16) + kh * kNBH * 1024;
+  // Stage base plus lane offset as one opaque register, so that the constant offsets of
+  // the individual reads fold into the LDS instructions.
+  auto pinned = [&](int st, int lane_off) {
+    uint32_t a = tiles_a + st * Dma::kTileBytes + lane_off;
+    asm("" : "+v"(a));
+    return (lds_ptr)(uintptr_t)(a);
+  };
+  // Probability exchange slot of (buffer, head group, hi/lo): 16 bytes per lane, of which
+  // this wave owns bytes [8 kh, 8 kh + 8).
+  auto pslot = [&](int buf, int hg, int hl) {
+    return reinterpret_cast<__attribute__((address_space(3))) char*>(lds_addr_of(pxchg)) +
+           ((((buf * 2 + hh) * 2 + hg) * 2 + hl) * 64 + lane) * 16;
+  };
+  lds_f32x2* const red_own = (lds_f32x2*)(lds_addr_of(red)) + wid * 64 + lane;
+  lds_f32x2* const red_partner = (lds_f32x2*)(lds_addr_of(red)) + (wid ^ 1) * 64 + lane;
+
+  // S^T of this wave's 16 keys of a tile for both head groups; two accumulation chains per
+  // head group (even / odd contraction steps).
+  auto logits = [&](int st, f32x4 (&s)[2][2]) {
+    const lds_ptr kb = pinned(st, k_lane);
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) s[hg][0] = s[hg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const bf16x8 a = lds_load_bf16x8(kb + ks * 2048);
+      s[0][ks & 1] = mfma16x16x32_bf16(a, qf[0][ks], s[0][ks & 1]);
+      s[1][ks & 1] = mfma16x16x32_bf16(a, qf[1][ks], s[1][ks & 1]);
+    }
+  };
+  // y = x - m with x = logit * log2(e) * scale rounded to fp32, for this lane's keys
+  // 16 kh + 4 g + i of tile t (-inf past the last valid slot).  Rounding x before the
+  // subtraction (the select between them keeps the two from being fused) makes y exactly
+  // 0 for the key that defines the reference.
+  auto shifted = [&](const f32x4 (&s)[2][2], int t, const float (&m)[2], f32x4 (&y)[2]) {
+    const int slot0 = t * kKeysPerTile + 16 * kh + 4 * g;
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x =
+            slot0 + i < n_valid ? (s[hg][0][i] + s[hg][1][i]) * scale_log2 : -__builtin_inff();
+        y[hg][i] = x - m[hg];
+      }
+  };
+  auto max4 = [](const f32x4& y) {
+    return __builtin_fmaxf(__builtin_fmaxf(y[0], y[1]), __builtin_fmaxf(y[2], y[3]));
+  };
+  auto head_max = [](float m) {
+    m = __builtin_fmaxf(m, shfl_xor(m, 16));
+    return __builtin_fmaxf(m, shfl_xor(m, 32));
+  };
+  auto head_sum = [](float l) {
+    l += shfl_xor(l, 16);
+    return l + shfl_xor(l, 32);
+  };
+  // Probabilities p = 2^y of this wave's keys, summed into l_run, and written as bf16
+  // hi + lo pairs into this wave's half of the exchange slots.
+  auto probabilities = [&](const f32x4 (&y)[2], int buf, float (&l_run)[2], float (&ymax)[2]) {
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      ymax[hg] = __builtin_fmaxf(ymax[hg], max4(y[hg]));
+      f32x4 p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(y[hg][i]);
+      l_run[hg] += (p[0] + p[1]) + (p[2] + p[3]);
+      const bf16x4 hi = __builtin_convertvector(p, bf16x4);
+      const bf16x4 lo = __builtin_convertvector(p - __builtin_convertvector(hi, f32x4), bf16x4);
+      *(lds_i16x4*)(pslot(buf, hg, 0) + 8 * kh) = __builtin_bit_cast(i16x4, hi);
+      *(lds_i16x4*)(pslot(buf, hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+    }
+  };
+  auto read_probabilities = [&](int buf, bf16x8 (&phi)[2], bf16x8 (&plo)[2]) {
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      phi[hg] = lds_load_bf16x8((lds_ptr)pslot(buf, hg, 0));
+      plo[hg] = lds_load_bf16x8((lds_ptr)pslot(buf, hg, 1));
+    }
+  };
+  // O^T += V^T . P^T over the 32 keys of a tile, value half kh.
+  auto pv_tile = [&](int st, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2]) {
+    const lds_ptr vb = pinned(st, v_lane);
+#pragma unroll
+    for (int nb = 0; nb < kNBH; ++nb) {
+      const bf16x8 vt = tile_tr_block(vb, nb);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        oacc[hg][nb] = mfma16x16x32_bf16(vt, phi[hg], oacc[hg][nb]);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        oacc[hg][nb] = mfma16x16x32_bf16(vt, plo[hg], oacc[hg][nb]);
+    }
+  };
+
+  // One pass over all tiles.  DO_PV: accumulate O and the row sums against m_ref (taken
+  // from tile 0 when REF_FIRST); otherwise take the exact maximum logit of every head into
+  // m_ref.  Tile t lives in LDS stage t % 3.
+  auto run_pass = [&](auto do_pv, auto ref_first) {
+    constexpr bool DO_PV = decltype(do_pv)::value;
+    constexpr bool REF_FIRST = decltype(ref_first)::value;
+    const float zero_m[2] = {0.f, 0.f};
+    float ymax[2] = {-__builtin_inff(), -__builtin_inff()};
+    float l_run[2] = {0.f, 0.f};
+    if constexpr (DO_PV) {
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+        for (int nb = 0; nb < kNBH; ++nb) oacc[hg][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    Dma::issue(tiles, 0, 0, sel, n_valid, kv, ld_kv, v, ld_v);
+    if (n_tiles > 1) {
+      Dma::issue(tiles, 1, 1, sel, n_valid, kv, ld_kv, v, ld_v);
+      DSA_WAIT_VMCNT(Dma::kPerWave);
+    } else {
+      DSA_WAIT_VMCNT(0);
+    }
+    tile_barrier();  // tile 0 is in LDS
+    f32x4 s[2][2], y[2];
+    if (compute) logits(0, s);
+    if constexpr (DO_PV && REF_FIRST) {
+      // The pair's common reference: the maximum of tile 0 over both key halves.
+      if (compute) {
+        shifted(s, 0, zero_m, y);
+        *red_own = f32x2{head_max(max4(y[0])), head_max(max4(y[1]))};
+      }
+      DSA_WAIT_LGKMCNT0();
+      tile_barrier();
+      if (compute) {
+        const f32x2 other = *red_partner;
+        m_ref[0] = __builtin_fmaxf(head_max(max4(y[0])), other.x);
+        m_ref[1] = __builtin_fmaxf(head_max(max4(y[1])), other.y);
+      }
+    }
+    if (compute) {
+      if constexpr (DO_PV) {
+        shifted(s, 0, m_ref, y);
+        probabilities(y, 0, l_run, ymax);
+      } else {
+        shifted(s, 0, zero_m, y);
+        ymax[0] = max4(y[0]);
+        ymax[1] = max4(y[1]);
+      }
+    }
+    DSA_WAIT_VMCNT(0);
+    DSA_WAIT_LGKMCNT0();
+    tile_barrier();  // tile 1 is in LDS; tile 0's probabilities are exchanged
+    bf16x8 phi[2], plo[2];
+    if constexpr (DO_PV) {
+      if (compute) read_probabilities(0, phi, plo);
+    }
+    if (n_tiles > 2) Dma::issue(tiles, 2, 2, sel, n_valid, kv, ld_kv, v, ld_v);
+    int st_cur = 0, st_next = 1, st_after = 2;  // stages of tiles t, t + 1, t + 2
+    for (int t = 0; t + 1 < n_tiles; ++t) {
+      if (compute) {
+        logits(st_next, s);
+        if constexpr (DO_PV) {
+          shifted(s, t + 1, m_ref, y);
+          probabilities(y, (t + 1) & 1, l_run, ymax);
+          pv_tile(st_cur, phi, plo);
+        } else {
+          shifted(s, t + 1, zero_m, y);
+          ymax[0] = __builtin_fmaxf(ymax[0], max4(y[0]));
+          ymax[1] = __builtin_fmaxf(ymax[1], max4(y[1]));
+        }
+      }
+      DSA_WAIT_VMCNT(0);  // tile t + 2 (if any) has landed
+      DSA_WAIT_LGKMCNT0();
+      tile_barrier();  // tile t is consumed; tile t + 2 and tile t + 1's probabilities are visible
+      if (t + 3 < n_tiles) Dma::issue(tiles, st_cur, t + 3, sel, n_valid, kv, ld_kv, v, ld_v);
+      if constexpr (DO_PV) {
+        if (compute) read_probabilities((t + 1) & 1, phi, plo);
+      }
+      const int st_free = st_cur;
+      st_cur = st_next;
+      st_next = st_after;
+      st_after = st_free;
+    }
+    if constexpr (DO_PV) {
+      if (compute) pv_tile(st_cur, phi, plo);  // the last tile
+    }
+    // Combine the pair's halves: row sums (P.V pass) or maxima (max pass) per head.
+    if (compute) {
+      if constexpr (DO_PV) {
+        overflow |= __builtin_fmaxf(ymax[0], ymax[1]) > kRefHeadroomLog2;
+        *red_own = f32x2{head_sum(l_run[0]), head_sum(l_run[1])};
+      } else {
+        *red_own = f32x2{head_max(ymax[0]), head_max(ymax[1])};
+      }
+    }
+    DSA_WAIT_LGKMCNT0();
+    tile_barrier();
+    if (compute) {
+      const f32x2 other = *red_partner;
+      if constexpr (DO_PV) {
+        l_tot[0] = head_sum(l_run[0]) + other.x;
+        l_tot[1] = head_sum(l_run[1]) + other.y;
+      } else {
+        m_ref[0] = __builtin_fmaxf(head_max(ymax[0]), other.x);
+        m_ref[1] = __builtin_fmaxf(head_max(ymax[1]), other.y);
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    run_pass(std::true_type{}, std::true_type{});
+    if (__syncthreads_or(overflow)) {
+      // Rare: a logit far above tile 0's maximum.  Take the exact maximum, then redo.
+      run_pass(std::false_type{}, std::false_type{});
+      __syncthreads();
+      run_pass(std::true_type{}, std::false_type{});
+    }
+  }
+
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const int head = hh * 32 + hg * 16 + r16;
+    if (head >= h) continue;
+    const float inv = n_valid > 0 ? 1.0f / l_tot[hg] : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < kNBH; ++nb) {
+      const int dim = (kh * kNBH + nb) * 16 + 4 * g;
+      if constexpr (OUT_F32) {
+        float* orow = static_cast<float*>(o) + (row * h + head) * DV;
+        *reinterpret_cast<f32x4*>(orow + dim) = oacc[hg][nb] * inv;
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(o) + (row * h + head) * DV;
+        const f32x4 yv = oacc[hg][nb] * inv;
+        const uint32_t w0 = static_cast<uint32_t>(float_to_bf16_bits(yv[0])) |
+                            (static_cast<uint32_t>(float_to_bf16_bits(yv[1])) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(float_to_bf16_bits(yv[2])) |
+                            (static_cast<uint32_t>(float_to_bf16_bits(yv[3])) << 16);
+        *reinterpret_cast<uint2*>(orow + dim) = make_uint2(w0, w1);
+      }
+    }
+    if (kh == 0 && g == 0)
+      lse[row * h + head] =
+          n_valid > 0 ? (m_ref[hg] + __builtin_log2f(l_tot[hg])) * kLn2 : -__builtin_inff();
+  }
+}
+
 template <int DQK, int DV, bool SEP, bool F32>
 hipError_t launch_fwd_variant(const void* q, const void* kv, int64_t ld_kv, const void* v,
                               int64_t ld_v, const int32_t* idx, int k, void* o, float* lse,
                               int64_t nq, int64_t n_pools, int h, float scale,
                               hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, SEP, F32>), dim3(static_cast<unsigned>(nq)),
-                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
-                     ld_v, idx, k, o, lse, n_pools, h, scale * kLog2e);
+  if constexpr (pair_fits<DQK, DV, SEP>()) {
+    hipLaunchKernelGGL((attn_fwd_pair_kernel<DQK, DV, SEP, F32>),
+                       dim3(static_cast<unsigned>(nq)), dim3(kAttnThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), ld_kv,
+                       static_cast<const uint16_t*>(v), ld_v, idx, k, o, lse, n_pools, h,
+                       scale * kLog2e);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, SEP, F32>), dim3(static_cast<unsigned>(nq)),
+                       dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
+                       ld_v, idx, k, o, lse, n_pools, h, scale * kLog2e);
+  }
   return hipGetLastError();
 }
 
