@@ -222,7 +222,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 
 template <int DQK, int DV, bool SEPARATE_V, bool OUT_F32>
-__global__ __launch_bounds__(kAttnThreads) void attn_fwd_pair_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     void* __restrict__ o, float* __restrict__ lse, int64_t n_pools, int h,
@@ -372,6 +373,80 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_pair_kernel(
     }
   };
 
+  // Steady-state body of the P.V pass as an explicit software pipeline: the logits of tile
+  // t1 (stage st_k) and the P.V product of the previous tile (stage st_v, operands phi/plo)
+  // share the MFMA pipe.  Phase 1: one slot per contraction step, each with the two logit
+  // MFMAs of that step and half of a P.V block; key fragments are read two slots ahead,
+  // value fragments one block ahead.  Phase 2: the remaining P.V blocks, with the softmax
+  // of tile t1 (whose inputs are complete after phase 1) in four pieces between them.
+  // Scheduling fences keep the compiler from regrouping loads next to their uses.
+  auto fused_step = [&](int st_k, int st_v, int t1, const bf16x8 (&phi)[2],
+                        const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2]) {
+    static_assert(kKS % 2 == 0 && kKS / 2 <= kNBH, "pipeline shape");
+    const lds_ptr kb = pinned(st_k, k_lane);
+    const lds_ptr vb = pinned(st_v, v_lane);
+    bf16x8 ka[3], vf[2];
+    f32x4 s[2][2];
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) s[hg][0] = s[hg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ka[0] = lds_load_bf16x8(kb);
+    ka[1] = lds_load_bf16x8(kb + 2048);
+    vf[0] = tile_tr_block(vb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kKS; ++j) {
+      const int n = j / 2;
+      if (j + 2 < kKS) ka[(j + 2) % 3] = lds_load_bf16x8(kb + (j + 2) * 2048);
+      if ((j & 1) == 0 && n + 1 < kNBH) vf[(n + 1) & 1] = tile_tr_block(vb, n + 1);
+      s[0][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[0][j], s[0][j & 1]);
+      s[1][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[1][j], s[1][j & 1]);
+      const bf16x8(&pp)[2] = (j & 1) ? plo : phi;
+      oacc[0][n] = mfma16x16x32_bf16(vf[n & 1], pp[0], oacc[0][n]);
+      oacc[1][n] = mfma16x16x32_bf16(vf[n & 1], pp[1], oacc[1][n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Phase 2.
+    f32x4 y[2], p[2];
+    const int slot0 = t1 * kKeysPerTile + 16 * kh + 4 * g;
+    auto piece = [&](int idx) {
+      const int hg = idx >> 1;
+      if ((idx & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = slot0 + i < n_valid ? (s[hg][0][i] + s[hg][1][i]) * scale_log2
+                                              : -__builtin_inff();
+          y[hg][i] = x - m_ref[hg];
+        }
+        ymax[hg] = __builtin_fmaxf(ymax[hg], max4(y[hg]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[hg][i] = __builtin_amdgcn_exp2f(y[hg][i]);
+        l_run[hg] += (p[hg][0] + p[hg][1]) + (p[hg][2] + p[hg][3]);
+      } else {
+        const bf16x4 hi = __builtin_convertvector(p[hg], bf16x4);
+        const bf16x4 lo =
+            __builtin_convertvector(p[hg] - __builtin_convertvector(hi, f32x4), bf16x4);
+        *(lds_i16x4*)(pslot((t1 & 1), hg, 0) + 8 * kh) = __builtin_bit_cast(i16x4, hi);
+        *(lds_i16x4*)(pslot((t1 & 1), hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+      }
+    };
+    constexpr int n0 = kKS / 2;
+#pragma unroll
+    for (int n = n0; n < kNBH; ++n) {
+      if (n + 1 < kNBH) vf[(n + 1) & 1] = tile_tr_block(vb, n + 1);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], phi[hg], oacc[hg][n]);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], plo[hg], oacc[hg][n]);
+      const int idx = n - n0 - 1;
+      if (idx >= 0 && idx < 4) piece(idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int idx = kNBH - n0 - 1 < 0 ? 0 : kNBH - n0 - 1; idx < 4; ++idx) piece(idx);
+  };
+
   // One pass over all tiles.  DO_PV: accumulate O and the row sums against m_ref (taken
   // from tile 0 when REF_FIRST); otherwise take the exact maximum logit of every head into
   // m_ref.  Tile t lives in LDS stage t % 3.
@@ -432,12 +507,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_pair_kernel(
     int st_cur = 0, st_next = 1, st_after = 2;  // stages of tiles t, t + 1, t + 2
     for (int t = 0; t + 1 < n_tiles; ++t) {
       if (compute) {
-        logits(st_next, s);
         if constexpr (DO_PV) {
-          shifted(s, t + 1, m_ref, y);
-          probabilities(y, (t + 1) & 1, l_run, ymax);
-          pv_tile(st_cur, phi, plo);
+          fused_step(st_next, st_cur, t + 1, phi, plo, l_run, ymax);
         } else {
+          logits(st_next, s);
           shifted(s, t + 1, zero_m, y);
           ymax[0] = __builtin_fmaxf(ymax[0], max4(y[0]));
           ymax[1] = __builtin_fmaxf(ymax[1], max4(y[1]));
