@@ -22,32 +22,43 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
 // Compacts the valid slots of one selection row (0 <= idx < n_pools; -1 marks an empty
 // slot, and any other value is skipped the same way so that no gather leaves the table)
 // into sel[], in slot order, and returns their count.  All threads of the block call it.
+// Thread i takes the m = ceil(k / threads) consecutive slots [i m, i m + m), all loaded in
+// one memory round trip; a block prefix sum over the per-thread counts places them.
 __device__ inline int compact_selection(const int32_t* __restrict__ irow, int k,
                                         int64_t n_pools, int32_t* sel, int* wave_tmp) {
+  constexpr int kMaxPer = kMaxTopK / kAttnThreads;
+  constexpr int kWaves = kAttnThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  constexpr int kWaves = kAttnThreads / 64;
-  int base = 0;
-  for (int s0 = 0; s0 < k; s0 += kAttnThreads) {
-    const int s = s0 + threadIdx.x;
-    const int32_t v = s < k ? irow[s] : -1;
-    const bool valid = v >= 0 && v < n_pools;
-    const uint64_t ballot = __ballot(valid);
-    const int before = __popcll(ballot & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tmp[wid] = __popcll(ballot);
-    __syncthreads();
-    int off = base;
-    int tot = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = wave_tmp[w];
-      if (w < wid) off += c;
-      tot += c;
-    }
-    if (valid) sel[off + before] = v;
-    base += tot;
-    __syncthreads();
+  const int m = (k + kAttnThreads - 1) / kAttnThreads;
+  const int s0 = threadIdx.x * m;
+  int32_t v[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) v[i] = (i < m && s0 + i < k) ? irow[s0 + i] : -1;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) cnt += (v[i] >= 0 && v[i] < n_pools) ? 1 : 0;
+  int incl = cnt;  // inclusive prefix over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
-  return base;
+  if (lane == 63) wave_tmp[wid] = incl;
+  __syncthreads();
+  int off = incl - cnt;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = wave_tmp[w];
+    if (w < wid) off += c;
+    total += c;
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i)
+    if (v[i] >= 0 && v[i] < n_pools) sel[off++] = v[i];
+  __syncthreads();
+  return total;
 }
 
 // Waits until at most `n` vector-memory operations of this wave are outstanding (n < 64).
@@ -103,17 +114,32 @@ struct TileDma {
   static_assert(kChunksRow % 2 == 0 && kInstr % (kAttnThreads / 64) == 0, "tile split");
   static_assert(DEPTH >= 1 && DEPTH <= 3 && kPerWave * (DEPTH - 1) < 64, "vmcnt range");
 
+  // The table row this lane gathers for tile t (keys past the last valid slot repeat the
+  // last valid row).
+  __device__ __forceinline__ static int32_t row_of(int t, const int32_t* sel, int n_valid) {
+    int slot = t * kKeysPerTile + (threadIdx.x & (kKeysPerTile - 1));
+    slot = slot < n_valid ? slot : n_valid - 1;
+    return sel[slot];
+  }
+
   // Issues the loads of tile t into stage `stage` of `tiles`.
   __device__ __forceinline__ static void issue(uint8_t* tiles, int stage, int t,
                                                const int32_t* sel, int n_valid,
                                                const uint16_t* __restrict__ kv, int64_t ld_kv,
                                                const uint16_t* __restrict__ v, int64_t ld_v) {
+    issue_row(tiles, stage, row_of(t, sel, n_valid), kv, ld_kv, v, ld_v);
+  }
+
+  // Issues the loads of the tile whose rows (one per lane, see row_of) are `p` into stage
+  // `stage` of `tiles`.
+  __device__ __forceinline__ static void issue_row(uint8_t* tiles, int stage, int64_t p,
+                                                   const uint16_t* __restrict__ kv,
+                                                   int64_t ld_kv,
+                                                   const uint16_t* __restrict__ v,
+                                                   int64_t ld_v) {
     const int lane = threadIdx.x & 63;
     // Wave-uniform: keeps the LDS destinations (M0) in scalar registers.
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int slot = t * kKeysPerTile + (lane & (kKeysPerTile - 1));
-    slot = slot < n_valid ? slot : n_valid - 1;
-    const int64_t p = sel[slot];
     const uint32_t base = lds_addr_of(tiles) + stage * kTileBytes;
     if constexpr (!SEPARATE_V) {
       // One row pointer; the wave's loads are at constant column offsets from it.

@@ -250,10 +250,8 @@ void attn_fwd_pair_kernel(
   const int64_t row = blockIdx.x;
   const bool compute = hh * 32 < h;  // wave-uniform; waves without heads only gather
 
-  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
-  const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
-
-  // Queries of the two head groups as B operands (lane column = head).
+  // Queries of the two head groups as B operands (lane column = head), loaded before the
+  // selection row so that both loads share one memory round trip.
   bf16x8 qf[2][kKS];
 #pragma unroll
   for (int hg = 0; hg < 2; ++hg) {
@@ -264,6 +262,8 @@ void attn_fwd_pair_kernel(
     for (int ks = 0; ks < kKS; ++ks)
       qf[hg][ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32) : bf16x8_zero();
   }
+  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
+  const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
   DSA_WAIT_VMCNT(0);  // the tile pipeline's waits count only tile loads
 
   f32x4 oacc[2][kNBH];
@@ -380,7 +380,18 @@ void attn_fwd_pair_kernel(
   // value fragments one block ahead.  Phase 2: the remaining P.V blocks, with the softmax
   // of tile t1 (whose inputs are complete after phase 1) in four pieces between them.
   // Scheduling fences keep the compiler from regrouping loads next to their uses.
-  auto fused_step = [&](int st_k, int st_v, int t1, const bf16x8 (&phi)[2],
+  // The first fragments of a fused step, read ahead (right after the previous tile barrier)
+  // so that their latency overlaps the barrier's other work.
+  struct Ahead {
+    bf16x8 k0, k1, v0;
+  };
+  auto read_ahead = [&](int st_k, int st_v, Ahead& ah) {
+    const lds_ptr kb = pinned(st_k, k_lane);
+    ah.k0 = lds_load_bf16x8(kb);
+    ah.k1 = lds_load_bf16x8(kb + 2048);
+    ah.v0 = tile_tr_block(pinned(st_v, v_lane), 0);
+  };
+  auto fused_step = [&](int st_k, int st_v, int t1, const Ahead& ah, const bf16x8 (&phi)[2],
                         const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2]) {
     static_assert(kKS % 2 == 0 && kKS / 2 <= kNBH, "pipeline shape");
     const lds_ptr kb = pinned(st_k, k_lane);
@@ -389,9 +400,9 @@ void attn_fwd_pair_kernel(
     f32x4 s[2][2];
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) s[hg][0] = s[hg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ka[0] = lds_load_bf16x8(kb);
-    ka[1] = lds_load_bf16x8(kb + 2048);
-    vf[0] = tile_tr_block(vb, 0);
+    ka[0] = ah.k0;
+    ka[1] = ah.k1;
+    vf[0] = ah.v0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kKS; ++j) {
@@ -505,10 +516,17 @@ void attn_fwd_pair_kernel(
     }
     if (n_tiles > 2) Dma::issue(tiles, 2, 2, sel, n_valid, kv, ld_kv, v, ld_v);
     int st_cur = 0, st_next = 1, st_after = 2;  // stages of tiles t, t + 1, t + 2
+    Ahead ah;
+    if constexpr (DO_PV) {
+      if (compute && n_tiles > 1) read_ahead(st_next, st_cur, ah);
+    }
     for (int t = 0; t + 1 < n_tiles; ++t) {
+      // Row of the tile three ahead (clamped, so always a valid read), read now so that the
+      // load issue after the barrier does not wait for LDS.
+      const int32_t row3 = Dma::row_of(t + 3, sel, n_valid);
       if (compute) {
         if constexpr (DO_PV) {
-          fused_step(st_next, st_cur, t + 1, phi, plo, l_run, ymax);
+          fused_step(st_next, st_cur, t + 1, ah, phi, plo, l_run, ymax);
         } else {
           logits(st_next, s);
           shifted(s, t + 1, zero_m, y);
@@ -519,10 +537,13 @@ void attn_fwd_pair_kernel(
       DSA_WAIT_VMCNT(0);  // tile t + 2 (if any) has landed
       DSA_WAIT_LGKMCNT0();
       tile_barrier();  // tile t is consumed; tile t + 2 and tile t + 1's probabilities are visible
-      if (t + 3 < n_tiles) Dma::issue(tiles, st_cur, t + 3, sel, n_valid, kv, ld_kv, v, ld_v);
       if constexpr (DO_PV) {
-        if (compute) read_probabilities((t + 1) & 1, phi, plo);
+        if (compute) {
+          read_probabilities((t + 1) & 1, phi, plo);
+          if (t + 2 < n_tiles) read_ahead(st_after, st_next, ah);
+        }
       }
+      if (t + 3 < n_tiles) Dma::issue_row(tiles, st_cur, row3, kv, ld_kv, v, ld_v);
       const int st_free = st_cur;
       st_cur = st_next;
       st_next = st_after;
