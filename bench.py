@@ -84,7 +84,8 @@ def main():
     ld = ((p + 3) // 4) * 4
     if has_attn:
         q, kv, _ = I.attn_inputs(wl, dev)
-        o = torch.empty((n, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
+        o_dtype = torch.bfloat16 if wl.attn_out == "bf16" else torch.float32
+        o = torch.empty((n, wl.heads, wl.d_v), dtype=o_dtype, device=dev)
         lse = torch.empty((n, wl.heads), dtype=torch.float32, device=dev)
         ws = torch.empty(B.forward_chunked_workspace_bytes(p, chunk, k), dtype=torch.uint8,
                          device=dev)
@@ -150,8 +151,9 @@ def main():
     topk_bytes = 4.0 * pairs + 4.0 * n * k
     slots = valid_slots(0, n, p, k)
     row_bytes = 2 * wl.d_qk if has_attn else 0
-    attn_bytes = (row_bytes * slots + n * wl.heads * wl.d_qk * 2 + n * wl.heads * wl.d_v * 4 +
-                  n * k * 4) if has_attn else 0.0
+    o_bytes = 2 if wl.attn_out == "bf16" else 4
+    attn_bytes = (row_bytes * slots + n * wl.heads * wl.d_qk * 2 +
+                  n * wl.heads * wl.d_v * o_bytes + n * k * 4) if has_attn else 0.0
     attn_flop = 2.0 * wl.heads * (wl.d_qk + wl.d_v) * slots if has_attn else 0.0
     idx_peak = PEAK_FP8_TFLOPS if wl.index_dtype == "fp8" else PEAK_BF16_TFLOPS
 
@@ -197,6 +199,10 @@ def main():
         roof = {"kernel": "attn_fwd", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
 
+    if has_attn and "attn_bwd" in wl.phases:
+        phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_for_bwd(wl, q_i, k_i, w, dev),
+                                           args.steps, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, q_i, k_i, w, q if has_attn else None, kv if has_attn else None,
@@ -219,12 +225,70 @@ def main():
         "config": {"workload": wl.name, "n_tokens": n, "n_pools": p, "h_i": wl.h_i,
                    "d_i": wl.d_i, "index_dtype": wl.index_dtype, "topk": k,
                    "heads": wl.heads, "d_qk": wl.d_qk, "d_v": wl.d_v, "chunk": chunk,
-                   "attn_out": "fp32"},
+                   "attn_out": wl.attn_out},
         "roofline": roof,
         "phases": phases,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def idx_for_bwd(wl, q_i, k_i, w, dev):
+    """Selections of every query (one chunked forward pass keeping its indices)."""
+    import torch
+
+    from long_context_sparse_index_amd import binding as B
+
+    n, p, k, chunk = wl.n_tokens, wl.n_pools, wl.topk, wl.chunk
+    ld = ((p + 3) // 4) * 4
+    idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((chunk, ld), dtype=torch.float32, device=dev)
+    for t0, nq in chunk_ranges(n, chunk):
+        B.index_scores(q_i[t0:t0 + nq], k_i, w, scores[:nq], q_start=t0)
+        B.topk(scores[:nq], idx[t0:t0 + nq], q_start=t0, n_pools=p)
+    torch.cuda.synchronize()
+    return idx
+
+
+def time_backward(wl, q, kv, o, lse, idx, steps, stream):
+    """Times dsa_sparse_attn_bwd over the whole sequence (dQ, and dK / dV by fp32 atomics)
+    on the forward's outputs; flops count the recomputed logits, dP, dV, dQ and dK."""
+    import torch
+
+    from long_context_sparse_index_amd import binding as B
+    from long_context_sparse_index_amd import inputs as I
+
+    n, p = wl.n_tokens, wl.n_pools
+    B.sparse_attn_fwd(q, kv, idx, o, lse, scale=wl.scale, d_v=wl.d_v)
+    d_o = I.grad_output(wl, q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dkv = torch.zeros((p, wl.d_qk), dtype=torch.float32, device=q.device)
+    ws = torch.empty(B.sparse_attn_bwd_workspace_bytes(n, wl.heads), dtype=torch.uint8,
+                     device=q.device)
+
+    def run():
+        # V is the first d_v columns of the latent row: its gradient folds into dKV
+        dkv.zero_()
+        B.sparse_attn_bwd(q, kv, idx, o, lse, d_o, dq, dkv, scale=wl.scale, d_v=wl.d_v,
+                          ws=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    slots = valid_slots(0, n, p, wl.topk)
+    flop = 2.0 * wl.heads * (3 * wl.d_qk + 2 * wl.d_v) * slots
+    return {"ms_per_step": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+            "frac_of_mfma_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "tokens_per_s": n / (ms * 1e-3),
+            "note": "dsa_sparse_attn_bwd over all rows (dQ, dKV with dV folded in), timed "
+                    "with the zeroing of dKV, %d launches" % steps}
 
 
 def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):

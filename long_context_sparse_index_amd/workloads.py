@@ -33,6 +33,7 @@ class Workload:
     d_v: int = 0
     scale: float = 0.0
     chunk: int = 0
+    attn_out: str = "fp32"  # dtype of the attention output O ("fp32" or "bf16")
     phases: tuple = field(default=("indexer", "topk", "attn_fwd"))
     description: str = ""
 
@@ -78,8 +79,10 @@ WORKLOADS = {
             name="tp_share_1m",
             n_tokens=1048576, n_pools=262144, h_i=8, d_i=128, index_dtype="bf16", int_range=4,
             w_period=4, topk=2048, heads=64, d_qk=576, d_v=512, scale=_s(576), chunk=16384,
+            attn_out="bf16",
             description="One tensor-parallel rank's share of a 1M-token DSA layer: 8 of 32 "
-                        "indexer heads, top-2048, 64-head sparse MQA, chunk 16384"),
+                        "indexer heads, top-2048, 64-head sparse MQA, chunk 16384; O in bf16 "
+                        "(69 GB; fp32 would be 137 GB next to the 77 GB of queries)"),
     ]
 }
 
