@@ -40,7 +40,45 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="first run one plain device copy of this many GiB (a known-size "
+                         "kernel that calibrates the HBM byte counters of a profiler run)")
     return ap.parse_args()
+
+
+# Sources of each kernel whose HBM traffic a committed profile records: the profile is
+# used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "attn_common.hpp", "common.hpp"],
+    "indexer": ["indexer.hip", "common.hpp"],
+    "topk": ["topk.hip", "common.hpp"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "long_context_sparse_index_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter profile
+    (profiles/<kernel>_<workload>_traffic.md, a line 'traffic: {json}'), or None when there
+    is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+                if rec.get("source_hash") != kernel_source_hash(kernel):
+                    return None
+                return rec["bytes_per_launch"]
+    return None
 
 
 def chunk_ranges(n, chunk):
@@ -75,6 +113,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.load_library()
+    if args.copy_probe_gib > 0:
+        nb = int(args.copy_probe_gib * (1 << 30))
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes exactly nb bytes
+        torch.cuda.synchronize()
+        print("bench: copy probe of %d bytes done" % nb, file=sys.stderr, flush=True)
+        del src, dst
     n, p, k, chunk = wl.n_tokens, wl.n_pools, wl.topk, wl.chunk
     has_attn = wl.heads > 0
     print("bench: workload %s (N=%d, P=%d, chunk %d)" % (wl.name, n, p, chunk),
@@ -189,15 +236,18 @@ def main():
     if dom == "indexer":
         ach = tflops(idx_flop / n_launch, per_step["indexer"] / n_launch)
         roof = {"kernel": "indexer", "bound": "mfma", "achieved": ach, "peak": idx_peak,
-                "unit": "TFLOP/s", "frac": ach / idx_peak, "traffic": None}
+                "unit": "TFLOP/s", "frac": ach / idx_peak,
+                "traffic": recorded_traffic("indexer", wl.name)}
     elif dom == "topk":
         ach = gbs(topk_bytes / n_launch, per_step["topk"] / n_launch)
         roof = {"kernel": "topk", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": recorded_traffic("topk", wl.name)}
     else:
         ach = gbs(attn_bytes / n_launch, per_step["attn_fwd"] / n_launch)
         roof = {"kernel": "attn_fwd", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": recorded_traffic("attn_fwd", wl.name)}
 
     if has_attn and "attn_bwd" in wl.phases:
         phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_for_bwd(wl, q_i, k_i, w, dev),
