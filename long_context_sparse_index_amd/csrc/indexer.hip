@@ -6,8 +6,10 @@
 //
 // Tiling.  A block owns a tile of BQ queries x 256 pools; each of its 4 waves owns 64 pools
 // and keeps their key rows in registers as MFMA A operands for the whole head loop, since
-// the pooled key is shared by all indexer heads.  The queries of one head are staged in LDS
-// (double-buffered, one barrier per head) and read by all waves as B operands.  Each head's
+// the pooled key is shared by all indexer heads.  The queries of one head are gathered into
+// LDS by asynchronous global->LDS loads issued three heads ahead (four stages, one barrier
+// per head), so their memory latency hides behind three heads of MFMA work, and read by all
+// waves as B operands.  Each head's
 // 16x16 products are ReLU'd and added with the head weight into fp32 score registers, so
 // the per-head products never leave the register file.  Products are laid out
 // pool-major (MFMA rows = pools, columns = queries), which puts one query per lane column:
@@ -76,6 +78,17 @@ __device__ __forceinline__ f32x4 mfma_frag(typename FragT<FP8>::type a,
     return mfma16x16x32_bf16(a, b, c);
 }
 
+// One asynchronous 16-byte-per-lane global -> LDS load (lane l's 16 bytes land at LDS byte
+// address lds_addr + 16 l).  Written as inline assembly so that the compiler does not drain
+// every outstanding load before the next LDS read; the head loop waits for exactly the
+// loads it needs.
+__device__ __forceinline__ void idx_dma_16b(const void* src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// Waits until at most `n` vector-memory operations of this wave are outstanding (n < 64).
+#define IDX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
 // D: d_i; NB: 16-query column blocks per tile (BQ = 16 * NB); FP8: e4m3 operands.
 template <int D, int NB, bool FP8>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
@@ -89,14 +102,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   constexpr int kStepBytes = 4 * kFragBytes;       // bytes of one row per MFMA
   constexpr int kKS = kRowBytes / kStepBytes;      // MFMAs per head per tile
   constexpr int kBQ = 16 * NB;
-  constexpr int kLdsRow = kRowBytes + 16;          // padded LDS row of one query
-  constexpr int kChunksPerRow = kRowBytes / 16;
-  constexpr int kChunks = kBQ * kChunksPerRow;
-  constexpr int kChunksPerThread = (kChunks + kIdxThreads - 1) / kIdxThreads;
+  constexpr int kCpr = kRowBytes / 16;             // 16-byte chunks per query row
+  constexpr int kHeadBytes = kBQ * kRowBytes;      // one head's query tile in LDS
+  constexpr int kDmaPerHead = kHeadBytes / 1024;   // 1 KB global->LDS loads per head
+  // Loads are dealt to the waves round-robin; a wave issues at most kDmaPerWave per head.
+  constexpr int kDmaPerWave = (kDmaPerHead + kIdxWaves - 1) / kIdxWaves;
+  constexpr int kStages = 4;                       // heads staged ahead
   static_assert(kRowBytes % kStepBytes == 0, "d_i must fill whole MFMA steps");
+  static_assert(kHeadBytes % 1024 == 0, "query tile of whole 1 KB loads");
+  // Every wave that issues loads issues exactly kDmaPerWave per head (the waits count them).
+  static_assert(kDmaPerHead % kIdxWaves == 0 || kDmaPerHead < kIdxWaves, "even split");
+  static_assert(kDmaPerWave * (kStages - 1) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][kBQ * kLdsRow];
+  // Query tile of a head in LDS: row r, chunk c at chunk position c ^ swz(r), so that the 16
+  // rows read by one lane group at the same chunk hit 16 different 16-byte bank groups
+  // (rows are not padded: the global->LDS loads fill 1 KB contiguously).
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kStages * kHeadBytes];
   __shared__ float w_lds[kBQ * kMaxHeads];
+  auto swz = [](int r) {
+    if constexpr (kCpr >= 16) return r & 15;
+    else return (r / (16 / kCpr)) & (kCpr - 1);
+  };
 
   // XCD-aware remap: consecutive logical tiles (same query tile) land on one XCD.
   const int n_tiles = n_pool_tiles * n_query_tiles;
@@ -113,7 +139,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int64_t pw0 = p0 + wid * kPoolsPerWave;
@@ -138,30 +164,25 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       kf[mb][ks] = ok ? load_frag<FP8>(kp + ks * kStepBytes) : zero_frag<FP8>();
   }
 
-  u32x4 pre[kChunksPerThread];
-  auto load_q = [&](int j) {
+  // This lane's source rows for the query-tile loads: the wave's load i is the head's 1 KB
+  // load L = wid + 4 i (if L < kDmaPerHead); lane slot s = 64 L + lane -> row s / kCpr,
+  // position s % kCpr.
+  const uint8_t* dma_src[kDmaPerWave];
 #pragma unroll
-    for (int c = 0; c < kChunksPerThread; ++c) {
-      const int chunk = tid + c * kIdxThreads;
-      const int row = chunk / kChunksPerRow;
-      const int col = chunk - row * kChunksPerRow;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (chunk < kChunks && q0 + row < nq)
-        v = *reinterpret_cast<const u32x4*>(q + (q0 + row) * q_stride_b +
-                                            static_cast<int64_t>(j) * kRowBytes + col * 16);
-      pre[c] = v;
-    }
-  };
-  auto store_q = [&](int buf) {
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int slot = 64 * (wid + kIdxWaves * i) + lane;
+    const int row = (slot / kCpr) % kBQ;  // loads past the tile (not issued) stay in range
+    const int chunk = (slot % kCpr) ^ swz(row);
+    const int64_t qrow = q0 + row < nq ? q0 + row : nq - 1;  // rows past nq: any valid row
+    dma_src[i] = q + qrow * q_stride_b + chunk * 16;
+  }
+  const uint32_t q_lds_a = lds_addr_of(q_lds);
+  auto issue = [&](int j) {
 #pragma unroll
-    for (int c = 0; c < kChunksPerThread; ++c) {
-      const int chunk = tid + c * kIdxThreads;
-      if (chunk < kChunks) {
-        const int row = chunk / kChunksPerRow;
-        const int col = chunk - row * kChunksPerRow;
-        *reinterpret_cast<u32x4*>(&q_lds[buf][row * kLdsRow + col * 16]) = pre[c];
-      }
-    }
+    for (int i = 0; i < kDmaPerWave; ++i)
+      if (wid + kIdxWaves * i < kDmaPerHead)
+        idx_dma_16b(dma_src[i] + static_cast<int64_t>(j) * kRowBytes,
+                    q_lds_a + (j % kStages) * kHeadBytes + (wid + kIdxWaves * i) * 1024);
   };
 
   f32x4 sc[kMB][NB];
@@ -170,13 +191,25 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_q(0);
-  store_q(0);
-  __syncthreads();
+  for (int j = 0; j < kStages - 1 && j < h_i; ++j) issue(j);
+  // B-operand rows of this lane: query nb * 16 + r16 of the tile.
+  const lds_ptr qb = lds_ptr_of(q_lds);
   for (int j = 0; j < h_i; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < h_i) load_q(j + 1);
+    // Head j's loads (and the key rows before them) have landed for this wave.
+    const int ahead = h_i - 1 - j < kStages - 2 ? h_i - 1 - j : kStages - 2;
+    if (ahead >= 2) {
+      IDX_WAIT_VMCNT(2 * kDmaPerWave);
+    } else if (ahead == 1) {
+      IDX_WAIT_VMCNT(kDmaPerWave);
+    } else {
+      IDX_WAIT_VMCNT(0);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // head j's tile is in LDS for every wave; j - 1 consumed
+    asm volatile("" ::: "memory");
+    if (j + kStages - 1 < h_i) issue(j + kStages - 1);
     if (wave_live) {
+      const lds_ptr stage = qb + (j % kStages) * kHeadBytes;
       f32x4 acc[kMB][NB];
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
@@ -186,9 +219,22 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       for (int ks = 0; ks < kKS; ++ks) {
         Frag qf[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          qf[nb] = load_frag<FP8>(&q_lds[buf][(nb * 16 + r16) * kLdsRow + ks * kStepBytes +
-                                              g * kFragBytes]);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int row = nb * 16 + r16;
+          const int c0 = (ks * kStepBytes + g * kFragBytes) / 16;
+          if constexpr (FP8) {
+            const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+            const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                stage + row * kRowBytes + (((c0 + 1) ^ swz(row)) * 16));
+            for (int e = 0; e < 4; ++e) {
+              qf[nb][e] = lo[e];
+              qf[nb][4 + e] = hi[e];
+            }
+          } else {
+            qf[nb] = lds_load_bf16x8(stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+          }
+        }
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -206,8 +252,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
                                            sc[mb][nb][i]);
       }
     }
-    if (j + 1 < h_i) store_q(buf ^ 1);
-    __syncthreads();
   }
   if (!wave_live) return;
 
