@@ -23,13 +23,16 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+# Per-file device options.  The indexer's MFMA accumulators feed a VALU epilogue after every
+# head; in VGPRs (instead of accumulation registers) they need no copy-out first.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC] + DEVICE + COMMON + ["-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC] + DEVICE + EXTRA.get(src, []) + COMMON + ["-x", "hip", "-c", path, "-o", obj]
     else:
         cmd = [HIPCC] + COMMON + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -78,6 +78,14 @@ __device__ __forceinline__ f32x4 mfma_frag(typename FragT<FP8>::type a,
     return mfma16x16x32_bf16(a, b, c);
 }
 
+// max(x, 0) as one integer max on the bit pattern: an IEEE float with the sign bit set is
+// a negative int32 (-0 included) and becomes +0.  A float max would first spend an
+// instruction quieting signalling NaNs.
+__device__ __forceinline__ float relu_bits(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // One asynchronous 16-byte-per-lane global -> LDS load (lane l's 16 bytes land at LDS byte
 // address lds_addr + 16 l).  Written as inline assembly so that the compiler does not drain
 // every outstanding load before the next LDS read; the head loop waits for exactly the
@@ -145,11 +153,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int64_t pw0 = p0 + wid * kPoolsPerWave;
   const bool wave_live = pw0 < vis_last;
 
-  // Head weights of the tile's queries.
+  // Head weights of the tile's queries, stored [head][query] so that the 16 lanes of a group
+  // read 16 consecutive words.
   for (int i = tid; i < kBQ * h_i; i += kIdxThreads) {
     const int row = i / h_i;
     const int j = i - row * h_i;
-    w_lds[row * kMaxHeads + j] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
+    w_lds[j * kBQ + row] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
   }
 
   // This wave's pooled key rows, resident for all heads.
@@ -212,10 +221,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       const lds_ptr stage = qb + (j % kStages) * kHeadBytes;
       f32x4 acc[kMB][NB];
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         Frag qf[NB];
 #pragma unroll
@@ -238,18 +243,18 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb)  // the first step starts from a literal zero
+            acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
+                                         ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float wv = w_lds[(nb * 16 + r16) * kMaxHeads + j];
+        const float wv = w_lds[j * kBQ + nb * 16 + r16];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sc[mb][nb][i] = __builtin_fmaf(wv, __builtin_fmaxf(acc[mb][nb][i], 0.0f),
-                                           sc[mb][nb][i]);
+            sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
       }
     }
   }
