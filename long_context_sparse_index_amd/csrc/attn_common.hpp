@@ -204,6 +204,80 @@ struct TileDma {
   }
 };
 
+// Gather of 32 selected rows in 128-byte bands: wave w loads the rows of tile keys
+// 8w .. 8w + 7 (lane l: key 8w + l / 8), one load per 128-byte band of the row, so each load
+// instruction covers 8 rows x 128 contiguous bytes (eight whole cache lines of the 1152-byte
+// latent rows) instead of 32 rows x 32 bytes.  Layout of a tile:
+//   [key / 8][band][key % 8][position] x 16 bytes, chunk c of a band at position
+//   (c % 8) ^ swz(key), swz(key) = (key >> 1) & 7,
+// so the 16 keys read together by an MFMA operand load fall on 16 distinct 16-byte slots of
+// the 256-byte bank window.  DEPTH tiles are staged (see TileDma for the waits).
+template <int DQK, int DV, bool SEPARATE_V, int DEPTH>
+struct TileDmaBands {
+  static constexpr int kChunksQK = DQK / 8;
+  static constexpr int kChunksRow = kChunksQK + (SEPARATE_V ? DV / 8 : 0);
+  static constexpr int kBands = kChunksRow / 8;
+  static constexpr int kTileBytes = kChunksRow * kKeysPerTile * 16;
+  static constexpr int kGroupBytes = kBands * 1024;  // one key group of 8 rows
+  static constexpr int kVChunk = SEPARATE_V ? kChunksQK : 0;  // first chunk of V in a row
+  static constexpr int kPerWave = kBands;
+  static constexpr int kLdsBytes = DEPTH * kTileBytes;
+  static_assert(kChunksRow % 8 == 0 && kChunksQK % 8 == 0, "whole bands");
+  static_assert(kAttnThreads == 256, "four waves of 8 keys");
+  static_assert(DEPTH >= 1 && DEPTH <= 3 && kPerWave * (DEPTH - 1) < 64, "vmcnt range");
+
+  __device__ __forceinline__ static int swz(int key) { return (key >> 1) & 7; }
+
+  // Byte offset in a tile of chunk `c` (columns [8c, 8c + 8)) of tile key `key`.
+  __device__ __forceinline__ static int offset(int key, int c) {
+    return (key >> 3) * kGroupBytes + (c >> 3) * 1024 + (key & 7) * 128 +
+           (((c & 7) ^ swz(key)) << 4);
+  }
+
+  // The table row this lane gathers for tile t (keys past the last valid slot repeat the
+  // last valid row).
+  __device__ __forceinline__ static int32_t row_of(int t, const int32_t* sel, int n_valid) {
+    const int key = 8 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 3);
+    int slot = t * kKeysPerTile + key;
+    slot = slot < n_valid ? slot : n_valid - 1;
+    return sel[slot];
+  }
+
+  // Issues the loads of the tile whose row for this lane is `p` into stage `stage`.
+  __device__ __forceinline__ static void issue_row(uint8_t* tiles, int stage, int64_t p,
+                                                   const uint16_t* __restrict__ kv,
+                                                   int64_t ld_kv,
+                                                   const uint16_t* __restrict__ v,
+                                                   int64_t ld_v) {
+    const int lane = threadIdx.x & 63;
+    // Wave-uniform: keeps the LDS destinations (M0) in scalar registers.
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int key = 8 * wid + (lane >> 3);
+    const int pos = (lane & 7) ^ swz(key);  // chunk of each band this lane loads
+    const uint32_t base = lds_addr_of(tiles) + stage * kTileBytes + wid * kGroupBytes;
+    if constexpr (!SEPARATE_V) {
+      const uint16_t* rowp = kv + p * ld_kv + pos * 8;
+#pragma unroll
+      for (int b = 0; b < kBands; ++b) dma_16b(rowp + b * 64, base + b * 1024);
+    } else {
+#pragma unroll
+      for (int b = 0; b < kBands; ++b) {
+        const int c = 8 * b + pos;
+        const uint16_t* src =
+            c < kChunksQK ? kv + p * ld_kv + c * 8 : v + p * ld_v + (c - kChunksQK) * 8;
+        dma_16b(src, base + b * 1024);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void issue(uint8_t* tiles, int stage, int t,
+                                               const int32_t* sel, int n_valid,
+                                               const uint16_t* __restrict__ kv, int64_t ld_kv,
+                                               const uint16_t* __restrict__ v, int64_t ld_v) {
+    issue_row(tiles, stage, row_of(t, sel, n_valid), kv, ld_kv, v, ld_v);
+  }
+};
+
 // Byte offset in a tile of the 16-byte chunk holding columns [8c, 8c + 8) of tile key `key`.
 __device__ __forceinline__ int tile_off(int c, int key) { return (c * kKeysPerTile + key) * 16; }
 

@@ -26,6 +26,10 @@
 #include <type_traits>
 
 #include "attn_common.hpp"
+
+#ifndef DSA_PV_PHASE1
+#define DSA_PV_PHASE1 9
+#endif
 #include "launch.hpp"
 
 namespace dsa {
@@ -228,11 +232,14 @@ void attn_fwd_pair_kernel(
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     void* __restrict__ o, float* __restrict__ lse, int64_t n_pools, int h,
     float scale_log2) {
-  using Dma = TileDma<DQK, DV, SEPARATE_V, 3>;
+  using Dma = TileDmaBands<DQK, DV, SEPARATE_V, 3>;
   constexpr int kKS = DQK / 32;   // q . k MFMA steps
   constexpr int kNBH = DV / 32;   // 16-column output blocks per value half
   static_assert(DQK % 64 == 0 && DV % 32 == 0, "tile shapes");
   static_assert(pair_fits<DQK, DV, SEPARATE_V>(), "LDS budget");
+  // P.V blocks of the current tile done in phase 1 of the loop body (next to the next tile's
+  // logits); the rest go to phase 2, where they cover the softmax.
+  constexpr int kN1 = DSA_PV_PHASE1 < kKS / 2 ? DSA_PV_PHASE1 : kKS / 2;
 
   __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pxchg[kPairXchgBytes];
@@ -276,10 +283,25 @@ void attn_fwd_pair_kernel(
   bool overflow = false;
 
   const uint32_t tiles_a = lds_addr_of(tiles);
-  // Key rows 16 kh + r of chunk column 4 ks + g for the logits; transposed value blocks of
-  // value half kh for O^T.
-  const int k_lane = tile_off(g, 16 * kh + r16);
-  const int v_lane = tile_tr_lane_off(Dma::kVBase, g, r16) + kh * kNBH * 1024;
+  // Lane offsets in a tile.  Logits: key 16 kh + r, chunk 4 ks + g, i.e. band ks / 2 and
+  // in-band chunk 4 (ks % 2) + g: one base for even and one for odd ks.  Transposed value
+  // block nb of value half kh (columns 16 nb ..): lane i of group g reads key 4 g + i / 4,
+  // chunk 2 nb + (i % 4) / 2, half i % 2; band nb / 4, in-band chunk 2 (nb % 4) + ..., so one
+  // base per nb % 4; the keys 16 .. 31 of the second read sit two key groups further.
+  const int k_lane[2] = {Dma::offset(16 * kh + r16, g), Dma::offset(16 * kh + r16, 4 + g)};
+  int v_lane[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int key = 4 * g + (r16 >> 2);
+    v_lane[m] = Dma::offset(key, Dma::kVChunk + 2 * kh * kNBH + 2 * m + ((r16 & 3) >> 1)) +
+                (r16 & 1) * 8;
+  }
+  constexpr int kVHi = 2 * Dma::kGroupBytes;  // keys 16 + k vs k
+  // Transposed V operand of block nb (relative to value half kh) from the four bases.
+  auto vt_block = [&](const lds_ptr (&vb)[4], int nb) {
+    const lds_ptr lo = vb[nb & 3] + (nb >> 2) * 1024;
+    return join_tr(lds_read_tr16_at(lo), lds_read_tr16_at(lo + kVHi));
+  };
   // Stage base plus lane offset as one opaque register, so that the constant offsets of
   // the individual reads fold into the LDS instructions.
   auto pinned = [&](int st, int lane_off) {
@@ -299,12 +321,12 @@ void attn_fwd_pair_kernel(
   // S^T of this wave's 16 keys of a tile for both head groups; two accumulation chains per
   // head group (even / odd contraction steps).
   auto logits = [&](int st, f32x4 (&s)[2][2]) {
-    const lds_ptr kb = pinned(st, k_lane);
+    const lds_ptr kb[2] = {pinned(st, k_lane[0]), pinned(st, k_lane[1])};
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) s[hg][0] = s[hg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const bf16x8 a = lds_load_bf16x8(kb + ks * 2048);
+      const bf16x8 a = lds_load_bf16x8(kb[ks & 1] + (ks >> 1) * 1024);
       s[0][ks & 1] = mfma16x16x32_bf16(a, qf[0][ks], s[0][ks & 1]);
       s[1][ks & 1] = mfma16x16x32_bf16(a, qf[1][ks], s[1][ks & 1]);
     }
@@ -360,10 +382,11 @@ void attn_fwd_pair_kernel(
   };
   // O^T += V^T . P^T over the 32 keys of a tile, value half kh.
   auto pv_tile = [&](int st, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2]) {
-    const lds_ptr vb = pinned(st, v_lane);
+    const lds_ptr vb[4] = {pinned(st, v_lane[0]), pinned(st, v_lane[1]), pinned(st, v_lane[2]),
+                           pinned(st, v_lane[3])};
 #pragma unroll
     for (int nb = 0; nb < kNBH; ++nb) {
-      const bf16x8 vt = tile_tr_block(vb, nb);
+      const bf16x8 vt = vt_block(vb, nb);
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg)
         oacc[hg][nb] = mfma16x16x32_bf16(vt, phi[hg], oacc[hg][nb]);
@@ -386,16 +409,17 @@ void attn_fwd_pair_kernel(
     bf16x8 k0, k1, v0;
   };
   auto read_ahead = [&](int st_k, int st_v, Ahead& ah) {
-    const lds_ptr kb = pinned(st_k, k_lane);
-    ah.k0 = lds_load_bf16x8(kb);
-    ah.k1 = lds_load_bf16x8(kb + 2048);
-    ah.v0 = tile_tr_block(pinned(st_v, v_lane), 0);
+    ah.k0 = lds_load_bf16x8(pinned(st_k, k_lane[0]));
+    ah.k1 = lds_load_bf16x8(pinned(st_k, k_lane[1]));
+    const lds_ptr v0 = pinned(st_v, v_lane[0]);
+    ah.v0 = join_tr(lds_read_tr16_at(v0), lds_read_tr16_at(v0 + kVHi));
   };
   auto fused_step = [&](int st_k, int st_v, int t1, const Ahead& ah, const bf16x8 (&phi)[2],
                         const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2]) {
     static_assert(kKS % 2 == 0 && kKS / 2 <= kNBH, "pipeline shape");
-    const lds_ptr kb = pinned(st_k, k_lane);
-    const lds_ptr vb = pinned(st_v, v_lane);
+    const lds_ptr kb[2] = {pinned(st_k, k_lane[0]), pinned(st_k, k_lane[1])};
+    const lds_ptr vb[4] = {pinned(st_v, v_lane[0]), pinned(st_v, v_lane[1]),
+                           pinned(st_v, v_lane[2]), pinned(st_v, v_lane[3])};
     bf16x8 ka[3], vf[2];
     f32x4 s[2][2];
 #pragma unroll
@@ -407,13 +431,16 @@ void attn_fwd_pair_kernel(
 #pragma unroll
     for (int j = 0; j < kKS; ++j) {
       const int n = j / 2;
-      if (j + 2 < kKS) ka[(j + 2) % 3] = lds_load_bf16x8(kb + (j + 2) * 2048);
-      if ((j & 1) == 0 && n + 1 < kNBH) vf[(n + 1) & 1] = tile_tr_block(vb, n + 1);
+      const bool pv = n < kN1;  // slots 0 .. 2 kN1 - 1 also carry half a P.V block
+      if (j + 2 < kKS) ka[(j + 2) % 3] = lds_load_bf16x8(kb[j & 1] + ((j + 2) >> 1) * 1024);
+      if (pv && (j & 1) == 0 && n + 1 < kNBH) vf[(n + 1) & 1] = vt_block(vb, n + 1);
       s[0][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[0][j], s[0][j & 1]);
       s[1][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[1][j], s[1][j & 1]);
-      const bf16x8(&pp)[2] = (j & 1) ? plo : phi;
-      oacc[0][n] = mfma16x16x32_bf16(vf[n & 1], pp[0], oacc[0][n]);
-      oacc[1][n] = mfma16x16x32_bf16(vf[n & 1], pp[1], oacc[1][n]);
+      if (pv) {
+        const bf16x8(&pp)[2] = (j & 1) ? plo : phi;
+        oacc[0][n] = mfma16x16x32_bf16(vf[n & 1], pp[0], oacc[0][n]);
+        oacc[1][n] = mfma16x16x32_bf16(vf[n & 1], pp[1], oacc[1][n]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Phase 2.
@@ -440,22 +467,25 @@ void attn_fwd_pair_kernel(
         *(lds_i16x4*)(pslot((t1 & 1), hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
       }
     };
-    constexpr int n0 = kKS / 2;
+    // Pieces of the softmax go after phase-2 blocks n0 + 1, n0 + 1 + kSp, ... (kSp apart).
+    constexpr int n0 = kN1;
+    constexpr int kSp = (kNBH - n0 - 1) / 4 > 1 ? (kNBH - n0 - 1) / 4 : 1;
 #pragma unroll
     for (int n = n0; n < kNBH; ++n) {
-      if (n + 1 < kNBH) vf[(n + 1) & 1] = tile_tr_block(vb, n + 1);
+      if (n + 1 < kNBH) vf[(n + 1) & 1] = vt_block(vb, n + 1);
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg)
         oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], phi[hg], oacc[hg][n]);
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg)
         oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], plo[hg], oacc[hg][n]);
-      const int idx = n - n0 - 1;
-      if (idx >= 0 && idx < 4) piece(idx);
+      const int rel = n - n0 - 1;
+      if (rel >= 0 && rel % kSp == 0 && rel / kSp < 4) piece(rel / kSp);
       __builtin_amdgcn_sched_barrier(0);
     }
+    constexpr int kDone = kNBH - n0 - 1 <= 0 ? 0 : ((kNBH - n0 - 2) / kSp + 1 < 4 ? (kNBH - n0 - 2) / kSp + 1 : 4);
 #pragma unroll
-    for (int idx = kNBH - n0 - 1 < 0 ? 0 : kNBH - n0 - 1; idx < 4; ++idx) piece(idx);
+    for (int idx = kDone; idx < 4; ++idx) piece(idx);  // pieces that found no block
   };
 
   // One pass over all tiles.  DO_PV: accumulate O and the row sums against m_ref (taken
