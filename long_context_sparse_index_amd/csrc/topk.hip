@@ -6,15 +6,19 @@
 // first among equal scores, -1 in the slots beyond the visible count.
 //
 // One 1024-thread block per query row.  Scores are mapped to order-preserving 32-bit keys.
-// A most-significant-digit radix select (11, 11, 10 bits) finds the k-th largest key:
-// each pass histograms the next digit of the keys that match the digits fixed so far in an
-// LDS histogram, and a block-wide suffix scan picks the digit bin that holds the k-th
-// element.  The search stops early once the chosen bin is taken whole.  A last pass walks
-// the row in index order with a block-wide prefix scan (wave shuffles, then one LDS step),
-// which gives every key above the threshold a slot and hands the remaining slots to the
-// threshold-equal keys of lowest index, so ties resolve exactly as a stable full sort.  The
-// k winners are sorted in LDS by a bitonic network on (~key, index) and written out.
-// Rows with no more visible pools than k skip the select and sort the whole prefix.
+// Pass A streams the row into an LDS histogram of the top 12 key bits, and a block-wide
+// suffix scan picks the bin holding the k-th largest key.  When that bin is taken whole or
+// holds at most 4096 keys (the usual case), pass B streams the row once more and moves the
+// keys above the bin to the winner list and the bin's keys to an LDS candidate list, both
+// through LDS slot counters, so pass B needs no block-wide synchronisation.  The remaining
+// 20 key bits are then resolved over the candidates alone (two 10-bit digit histograms);
+// if more candidates share the exact threshold key than slots remain, a select on the
+// pool index among them keeps the lowest pools, so ties resolve exactly as a stable full
+// sort.  A bin too large for the list is resolved over the row itself, followed by a
+// pool-ordered pass (block-wide prefix scans) that gives the remaining slots to the
+// threshold-equal keys of lowest pool.  The k winners are sorted on (~key, pool) by a
+// bitonic network held in registers (lane shuffles within a wave, LDS across waves) and
+// written out.  Rows with no more visible pools than k sort the whole prefix.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -27,6 +31,7 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kMaxK = 4096;
 constexpr int kBins0 = 4096;  // first digit: the top 12 bits of the key
 constexpr int kCand = 4096;   // candidate list: keys of the first digit's threshold bin
+constexpr int kLoads = 2;     // float4 loads in flight per thread while streaming a row
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t index) {
   return (static_cast<uint64_t>(~key) << 32) | index;  // ascending = key desc, index asc
@@ -64,23 +69,82 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return res;
 }
 
-__device__ void bitonic_sort(uint64_t* buf, int n2) {
-  for (int size = 2; size <= n2; size <<= 1) {
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), mask, 64));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), mask, 64));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Ascending bitonic sort of buf[0, 1024 R).  Element i lives in a register of thread
+// (i >> (6 + log2 R) waves, i & 63 lanes), slot (i >> 6) & (R - 1): strides below 64 are lane
+// exchanges, strides below 64 R are register pairs, and only strides across waves go through
+// LDS, alternating between buf and alt so that one barrier per such stage suffices.
+template <int R>
+__device__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
+  constexpr int kLogR = R == 1 ? 0 : (R == 2 ? 1 : 2);
+  constexpr int kN = kTopkThreads * R;
+  static_assert(R == 1 || R == 2 || R == 4, "1, 2 or 4 keys per thread");
+  const int lane = threadIdx.x & 63;
+  const int wbase = (threadIdx.x >> 6) << (6 + kLogR);
+  uint64_t v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = buf[wbase | (j << 6) | lane];
+  bool to_alt = false;
+#pragma unroll
+  for (int size = 2; size <= kN; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n2 >> 1); i += kTopkThreads) {
-        const int pos = 2 * i - (i & (stride - 1));
-        const int partner = pos + stride;
-        const bool up = (pos & size) == 0;
-        const uint64_t a = buf[pos];
-        const uint64_t b = buf[partner];
-        if ((a > b) == up) {
-          buf[pos] = b;
-          buf[partner] = a;
+      if (stride >= 64 * R) {
+        uint64_t* x = to_alt ? alt : buf;
+        to_alt = !to_alt;
+#pragma unroll
+        for (int j = 0; j < R; ++j) x[wbase | (j << 6) | lane] = v[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int i = wbase | (j << 6) | lane;
+          const uint64_t p = x[i ^ stride];
+          const bool take_min = ((i & size) == 0) == ((i & stride) == 0);
+          v[j] = ((p < v[j]) == take_min) ? p : v[j];
+        }
+      } else if (stride >= 64) {
+        const int js = stride >> 6;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          if (j & js) continue;
+          const int i = wbase | (j << 6) | lane;
+          const uint64_t a = v[j], b = v[j | js];
+          const bool up = (i & size) == 0;
+          const bool sw = (b < a) == up;
+          v[j] = sw ? b : a;
+          v[j | js] = sw ? a : b;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int i = wbase | (j << 6) | lane;
+          const uint64_t p = shfl_xor_u64(v[j], stride);
+          const bool take_min = ((i & size) == 0) == ((i & stride) == 0);
+          v[j] = ((p < v[j]) == take_min) ? p : v[j];
         }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();  // the last LDS stage may still read buf
+#pragma unroll
+  for (int j = 0; j < R; ++j) buf[wbase | (j << 6) | lane] = v[j];
+  __syncthreads();
+}
+
+// Sorts buf[0, n2) ascending, n2 a power of two <= kMaxK; buf[n2, max(n2, 1024)) must hold
+// ~0 (padding sorts last).  alt is scratch of the same size.
+__device__ void sort_keys(uint64_t* buf, uint64_t* alt, int n2) {
+  if (n2 <= kTopkThreads)
+    bitonic_sort_regs<1>(buf, alt);
+  else if (n2 <= 2 * kTopkThreads)
+    bitonic_sort_regs<2>(buf, alt);
+  else
+    bitonic_sort_regs<4>(buf, alt);
 }
 
 __device__ __forceinline__ int next_pow2(int n) {
@@ -121,18 +185,19 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, int nbins, ui
   return bin;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_kernel(const float* __restrict__ scores,
                                                             int64_t ld, int64_t q_start,
                                                             int64_t n_pools, int k,
                                                             int32_t* __restrict__ idx) {
   // The first-digit histogram is dead before the candidate list is written: they share LDS.
-  __shared__ uint64_t cand[kCand];  // (key << 32) | pool, in pool order
+  __shared__ uint64_t cand[kCand];  // (key << 32) | pool
   __shared__ uint32_t hist[1024];   // 10-bit digit histograms
   __shared__ uint64_t buf[kMaxK];
   uint32_t* const hist0 = reinterpret_cast<uint32_t*>(cand);  // kBins0 counters
   static_assert(kBins0 * 4 <= kCand * 8, "first histogram fits the candidate list");
   __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
   __shared__ uint32_t pick[3];
+  __shared__ uint32_t fill[2];  // slots taken in buf and in cand
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -142,127 +207,140 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   int32_t* orow = idx + r * k;
 
   if (vis <= k) {
-    const int n2 = next_pow2(vis > 0 ? vis : 1);
+    const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
     for (int i = tid; i < n2; i += kTopkThreads)
       buf[i] = i < vis ? composite(float_order_key(srow[i]), static_cast<uint32_t>(i)) : ~0ull;
     __syncthreads();
-    bitonic_sort(buf, n2);
+    sort_keys(buf, cand, n2);
     for (int i = tid; i < k; i += kTopkThreads)
       orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
     return;
   }
 
   const int n4 = (vis + 3) >> 2;  // float4 groups; the row is padded to ld (a multiple of 4)
-  // Histogram of the keys of the row that match (prefix, mask), on bits [shift, shift + 10).
-  auto row_hist10 = [&](uint32_t prefix, uint32_t mask, int shift) {
-    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-    __syncthreads();
-    for (int i4 = tid; i4 < n4; i4 += kTopkThreads) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(srow + 4 * i4);
+  // Calls f(i4, v) for every float4 group of the row, kLoads loads in flight per thread.
+  // Groups past the row end carry keys with index >= vis, which f must skip.
+  auto stream_row = [&](auto&& f) {
+    for (int base = 0; base < n4; base += kLoads * kTopkThreads) {
+      f32x4 v[kLoads];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = float_order_key(v[e]);
-        if (4 * i4 + e < vis && (key & mask) == prefix)
-          atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
+      for (int u = 0; u < kLoads; ++u) {
+        const int i4 = base + u * kTopkThreads + tid;
+        v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) f(base + u * kTopkThreads + tid, v[u]);
     }
-    __syncthreads();
   };
 
   // Pass A: the top 12 bits of every visible key.
   for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
+  if (tid < 2) fill[tid] = 0u;
   __syncthreads();
-  for (int i4 = tid; i4 < n4; i4 += kTopkThreads) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(srow + 4 * i4);
+  stream_row([&](int i4, const f32x4& v) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (4 * i4 + e < vis) atomicAdd(&hist0[float_order_key(v[e]) >> 20], 1u);
-  }
+  });
   __syncthreads();
   uint32_t above0, in0;
   const uint32_t b0 = pick_bin(hist0, kBins0, static_cast<uint32_t>(k), wave_tmp, pick,
                                &above0, &in0);
   uint32_t prefix = b0 << 20, mask = 0xFFF00000u;
   int krem = k - static_cast<int>(above0);
-  // The bin is taken whole, or its keys fit the candidate list: one more pass over the row
-  // places every key above the bin and moves the bin's keys to the candidates.  Otherwise
-  // the remaining bits are resolved over the row itself.
   const bool whole = in0 == static_cast<uint32_t>(krem);
-  const bool use_cand = !whole && in0 <= static_cast<uint32_t>(kCand);
-  if (!whole && !use_cand) {
-    for (int shift = 10; shift >= 0; shift -= 10) {
-      row_hist10(prefix, mask, shift);
-      uint32_t above_bin, in_bin;
-      const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
-                                    &above_bin, &in_bin);
-      prefix |= bin << shift;
-      mask |= 0x3FFu << shift;
-      krem -= static_cast<int>(above_bin);
-      if (in_bin == static_cast<uint32_t>(krem)) break;
-    }
-  }
 
-  // Ordered pass over the row: keys above the threshold prefix take slots [0, k - krem) in
-  // pool order; keys equal to it take [k - krem, k) in pool order (lowest pools first), or
-  // with candidates, go to the candidate list in pool order.
-  const uint32_t n_gt = static_cast<uint32_t>(k - krem);
-  uint32_t run_gt = 0u, run_eq = 0u;
-  for (int base4 = 0; base4 < n4; base4 += kTopkThreads) {
-    const int i4 = base4 + tid;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (i4 < n4) v = *reinterpret_cast<const f32x4*>(srow + 4 * i4);
-    uint32_t keys[4];
-    uint32_t cgt = 0u, ceq = 0u;
-    uint32_t flags = 0u;  // bit e: above, bit 4+e: equal
+  if (whole || in0 <= static_cast<uint32_t>(kCand)) {
+    // Pass B, in any order: keys above the bin (and the bin's own when it is taken whole)
+    // are winners; the bin's keys otherwise go to the candidate list.  The final sort
+    // orders the winners, so slots come from LDS counters.
+    stream_row([&](int i4, const f32x4& v) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * i4 + e;
-      keys[e] = float_order_key(v[e]);
-      if (i4 < n4 && i < vis) {
-        const uint32_t mk = keys[e] & mask;
-        if (mk > prefix) {
-          flags |= 1u << e;
-          ++cgt;
-        } else if (mk == prefix) {
-          flags |= 1u << (4 + e);
-          ++ceq;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
+        const uint32_t key = float_order_key(v[e]);
+        const uint32_t d = key >> 20;
+        if (static_cast<int>(i) < vis && d >= b0) {
+          if (d > b0 || whole)
+            buf[atomicAdd(&fill[0], 1u)] = composite(key, i);  // < above0 + in0 (whole) <= k
+          else
+            cand[atomicAdd(&fill[1], 1u)] = (static_cast<uint64_t>(key) << 32) | i;  // < in0
         }
       }
-    }
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
-    uint32_t pos_gt = run_gt + (pre & 0xFFFFu);
-    uint32_t rank_eq = run_eq + (pre >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
-      if (flags & (1u << e)) {
-        buf[pos_gt++] = composite(keys[e], i);
-      } else if (flags & (1u << (4 + e))) {
-        if (use_cand)
-          cand[rank_eq] = (static_cast<uint64_t>(keys[e]) << 32) | i;  // rank_eq < in0
-        else if (rank_eq < static_cast<uint32_t>(krem))
-          buf[n_gt + rank_eq] = composite(keys[e], i);
-        ++rank_eq;
+    });
+    __syncthreads();
+    if (!whole) {
+      // The remaining 20 key bits over the candidates only.
+      const int nc = static_cast<int>(in0);
+      bool tied = false;
+      for (int shift = 10; shift >= 0; shift -= 10) {
+        for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+        __syncthreads();
+        for (int i = tid; i < nc; i += kTopkThreads) {
+          const uint32_t key = static_cast<uint32_t>(cand[i] >> 32);
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
+        }
+        __syncthreads();
+        uint32_t above_bin, in_bin;
+        const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
+                                      &above_bin, &in_bin);
+        prefix |= bin << shift;
+        mask |= 0x3FFu << shift;
+        krem -= static_cast<int>(above_bin);
+        tied = in_bin != static_cast<uint32_t>(krem);
+        if (!tied) break;
+      }
+      // More candidates carry the threshold key than slots remain: the lowest pools among
+      // them win.  Pools are distinct, so a select on ~pool (larger = lower pool) over
+      // 10-bit windows at bits 22, 12, 2 and 0 ends with exactly krem of them.
+      uint32_t pprefix = 0u, pmask = 0u;
+      if (tied) {
+        for (int shift = 22;; shift = shift > 2 ? shift - 10 : 0) {
+          for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+          __syncthreads();
+          for (int i = tid; i < nc; i += kTopkThreads) {
+            const uint64_t c = cand[i];
+            const uint32_t npool = ~static_cast<uint32_t>(c);
+            if (static_cast<uint32_t>(c >> 32) == prefix && (npool & pmask) == pprefix)
+              atomicAdd(&hist[(npool >> shift) & 0x3FFu], 1u);
+          }
+          __syncthreads();
+          uint32_t above_bin, in_bin;
+          const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp,
+                                        pick, &above_bin, &in_bin);
+          pprefix |= bin << shift;
+          pmask |= 0x3FFu << shift;
+          krem -= static_cast<int>(above_bin);
+          if (in_bin == static_cast<uint32_t>(krem) || shift == 0) break;
+        }
+      }
+      // Winners among the candidates: above the threshold prefix, or on it and (when tied)
+      // at or above the pool threshold.
+      for (int i = tid; i < nc; i += kTopkThreads) {
+        const uint64_t c = cand[i];
+        const uint32_t key = static_cast<uint32_t>(c >> 32);
+        const uint32_t pool = static_cast<uint32_t>(c);
+        const uint32_t mk = key & mask;
+        if (mk > prefix || (mk == prefix && (~pool & pmask) >= pprefix))
+          buf[atomicAdd(&fill[0], 1u)] = composite(key, pool);  // k winners in all
       }
     }
-    run_gt += tot & 0xFFFFu;
-    run_eq += tot >> 16;
-    if (run_gt >= n_gt && run_eq >= (use_cand ? in0 : static_cast<uint32_t>(krem)))
-      break;  // uniform
-  }
-
-  if (use_cand) {
-    __syncthreads();
-    // The remaining 20 bits over the candidates only.
-    const int nc = static_cast<int>(in0);
+  } else {
+    // The bin holds more keys than the candidate list: resolve the remaining bits over the
+    // row, then one ordered pass places the keys above the threshold and hands the krem
+    // slots left to the threshold-equal keys of lowest pool.
     for (int shift = 10; shift >= 0; shift -= 10) {
       for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
       __syncthreads();
-      for (int i = tid; i < nc; i += kTopkThreads) {
-        const uint32_t key = static_cast<uint32_t>(cand[i] >> 32);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
-      }
+      stream_row([&](int i4, const f32x4& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = float_order_key(v[e]);
+          if (4 * i4 + e < vis && (key & mask) == prefix)
+            atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
+        }
+      });
       __syncthreads();
       uint32_t above_bin, in_bin;
       const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
@@ -272,50 +350,62 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       krem -= static_cast<int>(above_bin);
       if (in_bin == static_cast<uint32_t>(krem)) break;
     }
-    // Ordered selection among the candidates (in pool order; thread t takes the entries
-    // [4 t, 4 t + 4)): above the prefix -> the slots after the row's winners, equal -> the
-    // last krem slots, lowest pools first.
-    const uint32_t base_gt = n_gt;
-    const uint32_t n_gt_all = static_cast<uint32_t>(k - krem);
-    uint32_t cgt = 0u, ceq = 0u, flags = 0u;
+    // Thread t takes the 16 consecutive keys [16 t, 16 t + 16) of each 16384-key group, so a
+    // block scan of the per-thread counts gives pool-ordered ranks.
+    constexpr int kU = 4;  // float4 per thread per group
+    const uint32_t n_gt = static_cast<uint32_t>(k - krem);
+    uint32_t run_gt = 0u, run_eq = 0u;
+    for (int base4 = 0; base4 < n4; base4 += kU * kTopkThreads) {
+      f32x4 cur[kU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * tid + e;
-      if (i < nc) {
-        const uint32_t mk = static_cast<uint32_t>(cand[i] >> 32) & mask;
-        if (mk > prefix) {
-          flags |= 1u << e;
-          ++cgt;
-        } else if (mk == prefix) {
-          flags |= 1u << (4 + e);
-          ++ceq;
+      for (int u = 0; u < kU; ++u) {
+        const int i4 = base4 + kU * tid + u;
+        cur[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      uint32_t cgt = 0u, ceq = 0u;
+      uint32_t flags = 0u;  // bit e: above, bit 16 + e: equal
+#pragma unroll
+      for (int e = 0; e < 4 * kU; ++e) {
+        const int i = 4 * (base4 + kU * tid) + e;
+        const uint32_t mk = float_order_key(cur[e >> 2][e & 3]) & mask;
+        if (i < vis) {
+          if (mk > prefix) {
+            flags |= 1u << e;
+            ++cgt;
+          } else if (mk == prefix) {
+            flags |= 1u << (16 + e);
+            ++ceq;
+          }
         }
       }
-    }
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
-    uint32_t pos_gt = base_gt + (pre & 0xFFFFu);
-    uint32_t rank_eq = pre >> 16;
+      uint32_t tot;
+      const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
+      if (flags != 0u) {
+        uint32_t pos_gt = run_gt + (pre & 0xFFFFu);
+        uint32_t rank_eq = run_eq + (pre >> 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * tid + e;
-      if (i >= nc) continue;
-      const uint64_t c = cand[i];
-      const uint32_t key = static_cast<uint32_t>(c >> 32);
-      const uint32_t pool = static_cast<uint32_t>(c);
-      if (flags & (1u << e)) {
-        buf[pos_gt++] = composite(key, pool);
-      } else if (flags & (1u << (4 + e))) {
-        if (rank_eq < static_cast<uint32_t>(krem)) buf[n_gt_all + rank_eq] = composite(key, pool);
-        ++rank_eq;
+        for (int e = 0; e < 4 * kU; ++e) {
+          const uint32_t i = static_cast<uint32_t>(4 * (base4 + kU * tid) + e);
+          const uint32_t key = float_order_key(cur[e >> 2][e & 3]);
+          if (flags & (1u << e)) {
+            buf[pos_gt++] = composite(key, i);
+          } else if (flags & (1u << (16 + e))) {
+            if (rank_eq < static_cast<uint32_t>(krem)) buf[n_gt + rank_eq] = composite(key, i);
+            ++rank_eq;
+          }
+        }
       }
+      run_gt += tot & 0xFFFFu;
+      run_eq += tot >> 16;
+      if (run_gt >= n_gt && run_eq >= static_cast<uint32_t>(krem)) break;  // uniform
     }
   }
 
-  const int n2 = next_pow2(k);
+  const int n2 = max(next_pow2(k), kTopkThreads);
   for (int i = k + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
   __syncthreads();
-  bitonic_sort(buf, n2);
+  sort_keys(buf, cand, n2);
   for (int i = tid; i < k; i += kTopkThreads)
     orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
 }
