@@ -69,61 +69,96 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return res;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), mask, 64));
-  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), mask, 64));
+// Value of lane (lane ^ LS) of the wave, by VALU cross-lane moves: DPP quad permutes for 1
+// and 2, a half-row mirror (lane ^ 7) then a quad reversal (lane ^ 3) for 4, a row rotation
+// by 8 for 8, and the gfx950 row and half-wave swaps for 16 and 32.
+template <int LS>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  if constexpr (LS == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (LS == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (LS == 4) {
+    const uint32_t m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    return __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);               // quad_perm [3,2,1,0]
+  } else if constexpr (LS == 8) {
+    return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (LS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(LS == 32, "lane strides 1..32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
+template <int LS>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v) {
+  const uint32_t lo = lane_xor<LS>(static_cast<uint32_t>(v));
+  const uint32_t hi = lane_xor<LS>(static_cast<uint32_t>(v >> 32));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Ascending bitonic sort of buf[0, 1024 R).  Element i lives in a register of thread
-// (i >> (6 + log2 R) waves, i & 63 lanes), slot (i >> 6) & (R - 1): strides below 64 are lane
-// exchanges, strides below 64 R are register pairs, and only strides across waves go through
-// LDS, alternating between buf and alt so that one barrier per such stage suffices.
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int ls) {
+  switch (ls) {
+    case 1: return lane_xor_u64<1>(v);
+    case 2: return lane_xor_u64<2>(v);
+    case 4: return lane_xor_u64<4>(v);
+    case 8: return lane_xor_u64<8>(v);
+    case 16: return lane_xor_u64<16>(v);
+    default: return lane_xor_u64<32>(v);
+  }
+}
+
+// Ascending bitonic sort of buf[0, 1024 R).  Index bits [0, log2 R) select one of the R
+// registers of a thread, the next 6 bits the lane and the top 4 bits the wave, so the most
+// frequent (smallest) strides are register pairs, the next ones VALU lane exchanges, and
+// only strides across waves go through LDS, alternating between buf and alt so that one
+// barrier per such stage suffices.
 template <int R>
 __device__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
   constexpr int kLogR = R == 1 ? 0 : (R == 2 ? 1 : 2);
   constexpr int kN = kTopkThreads * R;
   static_assert(R == 1 || R == 2 || R == 4, "1, 2 or 4 keys per thread");
   const int lane = threadIdx.x & 63;
-  const int wbase = (threadIdx.x >> 6) << (6 + kLogR);
+  const int base = ((threadIdx.x >> 6) << (6 + kLogR)) | (lane << kLogR);
   uint64_t v[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) v[j] = buf[wbase | (j << 6) | lane];
+  for (int j = 0; j < R; ++j) v[j] = buf[base | j];
   bool to_alt = false;
 #pragma unroll
   for (int size = 2; size <= kN; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 64 * R) {
-        uint64_t* x = to_alt ? alt : buf;
-        to_alt = !to_alt;
-#pragma unroll
-        for (int j = 0; j < R; ++j) x[wbase | (j << 6) | lane] = v[j];
-        __syncthreads();
+      if (stride < R) {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-          const int i = wbase | (j << 6) | lane;
-          const uint64_t p = x[i ^ stride];
+          if (j & stride) continue;
+          const uint64_t a = v[j], b = v[j | stride];
+          const bool up = ((base | j) & size) == 0;
+          const bool sw = (b < a) == up;
+          v[j] = sw ? b : a;
+          v[j | stride] = sw ? a : b;
+        }
+      } else if (stride < 64 * R) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int i = base | j;
+          const uint64_t p = lane_xor_u64(v[j], stride >> kLogR);
           const bool take_min = ((i & size) == 0) == ((i & stride) == 0);
           v[j] = ((p < v[j]) == take_min) ? p : v[j];
         }
-      } else if (stride >= 64) {
-        const int js = stride >> 6;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          if (j & js) continue;
-          const int i = wbase | (j << 6) | lane;
-          const uint64_t a = v[j], b = v[j | js];
-          const bool up = (i & size) == 0;
-          const bool sw = (b < a) == up;
-          v[j] = sw ? b : a;
-          v[j | js] = sw ? a : b;
-        }
       } else {
+        uint64_t* x = to_alt ? alt : buf;
+        to_alt = !to_alt;
+#pragma unroll
+        for (int j = 0; j < R; ++j) x[base | j] = v[j];
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-          const int i = wbase | (j << 6) | lane;
-          const uint64_t p = shfl_xor_u64(v[j], stride);
+          const int i = base | j;
+          const uint64_t p = x[i ^ stride];
           const bool take_min = ((i & size) == 0) == ((i & stride) == 0);
           v[j] = ((p < v[j]) == take_min) ? p : v[j];
         }
@@ -132,7 +167,7 @@ __device__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
   }
   __syncthreads();  // the last LDS stage may still read buf
 #pragma unroll
-  for (int j = 0; j < R; ++j) buf[wbase | (j << 6) | lane] = v[j];
+  for (int j = 0; j < R; ++j) buf[base | j] = v[j];
   __syncthreads();
 }
 
