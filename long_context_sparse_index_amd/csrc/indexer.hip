@@ -201,6 +201,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int j = 0; j < kStages - 1 && j < h_i; ++j) issue(j);
+  // The key rows and the first heads' loads land together.  Waiting for them here, once,
+  // also tells the compiler that the key registers are complete before the head loop;
+  // otherwise it would wait for every outstanding load (the prefetched heads included) at
+  // their first use in each iteration.
+  IDX_WAIT_VMCNT(0);
   // B-operand rows of this lane: query nb * 16 + r16 of the tile.
   const lds_ptr qb = lds_ptr_of(q_lds);
   for (int j = 0; j < h_i; ++j) {
