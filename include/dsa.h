@@ -130,7 +130,9 @@ size_t dsa_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k);
  *   idx  [nq, k] int32 in [-1, n_pools); -1 slots may sit anywhere.
  *   o    [nq, h, d_v] output, fp32 (o_dtype DSA_DTYPE_F32) or bf16 (DSA_DTYPE_BF16, the
  *        fp32 result rounded to nearest even once);  lse [nq, h] fp32 (natural log).
- *   Supported: (d_qk, d_v) in {(128, 128), (576, 512)}, 1 <= h <= 64, 1 <= k <= 4096.
+ *   Supported: (d_qk, d_v) in {(128, 128), (576, 512), (512, 512), (256, 256)} (the last two
+ *   are the latent row without its rotary columns, NoPE, full and half width),
+ *   1 <= h <= 64, 1 <= k <= 4096 (any k, e.g. 2051).
  *   Slots holding a value outside [-1, n_pools) are skipped like -1 (never dereferenced).
  * Arithmetic: bf16 MFMA for q.K with fp32 accumulation, fp32 online softmax; each
  * probability enters the P.V MFMA as a pair of bf16 values (its rounding and the rounding

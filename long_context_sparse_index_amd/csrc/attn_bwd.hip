@@ -436,6 +436,8 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, 
                                           stream)
   if (d_qk == 128 && d_v == 128) DSA_BWD(128, 128);
   if (d_qk == 576 && d_v == 512) DSA_BWD(576, 512);
+  if (d_qk == 512 && d_v == 512) DSA_BWD(512, 512);
+  if (d_qk == 256 && d_v == 256) DSA_BWD(256, 256);
 #undef DSA_BWD
   return hipErrorInvalidValue;
 }

@@ -680,8 +680,12 @@ hipError_t launch_fwd_t(const void* q, const void* kv, int64_t ld_kv, const void
 
 }  // namespace
 
+// Latent row shapes with a kernel: 128/128; 576/512 (the DeepSeek-V3.2 shape: 512 value
+// columns plus 64 rotary columns of the key); and the same latent rows without the rotary
+// part (NoPE, V = the whole key row), full and half width: 512/512 and 256/256.
 bool attn_shape_supported(int d_qk, int d_v) {
-  return (d_qk == 128 && d_v == 128) || (d_qk == 576 && d_v == 512);
+  return (d_qk == 128 && d_v == 128) || (d_qk == 576 && d_v == 512) ||
+         (d_qk == 512 && d_v == 512) || (d_qk == 256 && d_v == 256);
 }
 
 int attn_max_k() { return kMaxTopK; }
@@ -697,6 +701,12 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* kv, int64_t ld_kv, 
                                   scale, stream);
   if (d_qk == 576 && d_v == 512)
     return launch_fwd_t<576, 512>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, nq, n_pools, h,
+                                  scale, stream);
+  if (d_qk == 512 && d_v == 512)
+    return launch_fwd_t<512, 512>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, nq, n_pools, h,
+                                  scale, stream);
+  if (d_qk == 256 && d_v == 256)
+    return launch_fwd_t<256, 256>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, nq, n_pools, h,
                                   scale, stream);
   return hipErrorInvalidValue;
 }

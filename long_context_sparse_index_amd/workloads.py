@@ -76,6 +76,20 @@ WORKLOADS = {
             description="Sparse attention forward + backward at 64k tokens, indices from the "
                         "128k-rule indexer, 64 heads over 576/512 latent rows"),
         Workload(
+            name="nope_16k",
+            n_tokens=16384, n_pools=4096, h_i=8, d_i=64, index_dtype="bf16", int_range=4,
+            w_period=4, topk=2051, heads=16, d_qk=512, d_v=512, scale=_s(512), chunk=4096,
+            phases=("indexer", "topk", "attn_fwd", "attn_bwd"),
+            description="Flash-native shapes, small: top-2051 (not a multiple of the 32-key "
+                        "tile), 16 heads over 512-wide NoPE latent rows (V = the whole row), "
+                        "chunk 4096"),
+        Workload(
+            name="flash_nope_128k",
+            n_tokens=131072, n_pools=32768, h_i=32, d_i=128, index_dtype="bf16", int_range=4,
+            w_period=4, topk=2051, heads=64, d_qk=512, d_v=512, scale=_s(512), chunk=8192,
+            description="DSA forward at 128k with Flash-native shapes: top-2051 and 64-head "
+                        "sparse MQA over 512-wide NoPE latent rows (no padding to 576/512)"),
+        Workload(
             name="tp_share_1m",
             n_tokens=1048576, n_pools=262144, h_i=8, d_i=128, index_dtype="bf16", int_range=4,
             w_period=4, topk=2048, heads=64, d_qk=576, d_v=512, scale=_s(576), chunk=16384,

@@ -75,10 +75,36 @@ def test_backward_latent_576_random_selection(gpu, h):
     assert np.abs(dq[1].cpu().numpy()).max() <= 1e-4 * float(np.sqrt(np.mean(rq * rq)))
 
 
-def test_backward_64k_full_size(gpu):
-    wl = W.WORKLOADS["fwd_bwd_64k"]
+@pytest.mark.parametrize("d", [256, 512])
+def test_backward_nope_latent_rows(gpu, d):
+    """NoPE latent rows (d_qk = d_v = d, V the whole row) with k = 2051."""
+    say("case: backward NoPE %d/%d random idx" % (d, d))
+    nq, p, k, h = 32, 3000, 2051, 64
+    g = torch.Generator(device=gpu).manual_seed(41 + d)
+    q = torch.randn((nq, h, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    kv = torch.randn((p, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    d_o = torch.randn((nq, h, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    idx = torch.argsort(torch.rand((nq, p), generator=g, device=gpu), dim=1)[:, :k]
+    idx = idx.to(torch.int32).contiguous()
+    idx[torch.rand((nq, k), generator=g, device=gpu) < 0.1] = -1
+    idx[0] = -1
+    idx[2, 40:] = -1
+    scale = 1.0 / float(np.sqrt(d))
+    dq, dkv, dv = _run_bwd(q, kv, idx, d_o, scale, d, separate_dv=True)
+    kv_h = host_bits(kv)
+    rq, rk, rv = oracle.sparse_attn_bwd(host_bits(q), kv_h, idx.cpu().numpy(), host_bits(d_o),
+                                        scale, v_bits=kv_h[:, :d].copy(), d_v=d)
+    assert_close(dq.cpu().numpy(), rq, "dQ")
+    assert_close(dkv.cpu().numpy(), rk, "dK")
+    assert_close(dv.cpu().numpy(), rv, "dV")
+    assert np.all(dq[0].cpu().numpy() == 0.0)
+
+
+@pytest.mark.parametrize("name", ["fwd_bwd_64k", "nope_16k"])
+def test_backward_full_size(gpu, name):
+    wl = W.WORKLOADS[name]
     n, p, k = wl.n_tokens, wl.n_pools, wl.topk
-    say("case: backward fwd_bwd_64k full size (N=%d, P=%d)" % (n, p))
+    say("case: backward %s full size (N=%d, P=%d)" % (name, n, p))
     q_i, k_i, w = I.index_inputs(wl, gpu)
     q, kv, _ = I.attn_inputs(wl, gpu)
     d_o = I.grad_output(wl, gpu)

@@ -225,6 +225,39 @@ def test_attention_latent_576_random_selection(gpu, h):
     assert np.max(np.abs(lse_h[fin] - rl[fin])) < 1e-4
 
 
+@pytest.mark.parametrize("separate_v", [False, True])
+@pytest.mark.parametrize("h", [64, 24])
+@pytest.mark.parametrize("d", [256, 512])
+def test_attention_nope_latent_rows(gpu, d, h, separate_v):
+    """Latent rows without their rotary columns (NoPE): d_qk = d_v = d, V the whole row (or
+    a separate table), k = 2051, not a multiple of the 32-key tile."""
+    say("case: attention NoPE %d/%d random idx h=%d separate_v=%s" % (d, d, h, separate_v))
+    nq, p, k = 40, 4096, 2051
+    g = torch.Generator(device=gpu).manual_seed(31 + d + h + int(separate_v))
+    q = torch.randn((nq, h, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    kv = torch.randn((p, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    v = torch.randn((p, d), generator=g, device=gpu, dtype=torch.bfloat16) if separate_v \
+        else None
+    perm = torch.argsort(torch.rand((nq, p), generator=g, device=gpu), dim=1)[:, :k]
+    idx = perm.to(torch.int32).contiguous()
+    idx[torch.rand((nq, k), generator=g, device=gpu) < 0.1] = -1
+    idx[0] = -1  # a row with no valid slot
+    idx[1, :] = -1
+    idx[1, 2050] = 9  # one valid slot, in the partial last tile
+    idx[2, 33:] = -1
+    scale = 1.0 / float(np.sqrt(d))
+    o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=scale, d_v=d, v=v)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(q, kv, idx, scale, d, v=v)
+    assert_close(o.cpu().numpy(), ro, "O")
+    assert np.all(o[0].cpu().numpy() == 0) and np.all(np.isneginf(lse[0].cpu().numpy()))
+    vt = v if separate_v else kv
+    assert np.array_equal(o[1].cpu().numpy(), np.broadcast_to(
+        vt[9, :d].float().cpu().numpy(), (h, d)))  # one slot: O is that value row
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(lse.cpu().numpy()[fin] - rl[fin])) < 1e-4
+
+
 def test_attention_logit_far_above_first_tile(gpu):
     """The forward takes each head's softmax reference from the first gathered tile; a
     later logit more than 2^64 above it must trigger the exact-maximum redo of the token."""
@@ -335,6 +368,15 @@ def _full_size_forward(gpu, wl, check_rows):
 def test_fwd_128k_full_size_sampled(gpu):
     wl = W.WORKLOADS["fwd_128k"]
     say("case: fwd_128k full size (N=%d), chunk %d" % (wl.n_tokens, wl.chunk))
+    _full_size_forward(gpu, wl, I.sample_rows(wl, n_uniform=24))
+
+
+@pytest.mark.parametrize("name", ["nope_16k", "flash_nope_128k"])
+def test_flash_native_full_size_sampled(gpu, name):
+    """Flash-native shapes end to end: top-2051 indices bit-exact and NoPE 512/512 attention
+    within tolerance on sampled rows, all rows structurally checked."""
+    wl = W.WORKLOADS[name]
+    say("case: %s full size (N=%d), chunk %d" % (name, wl.n_tokens, wl.chunk))
     _full_size_forward(gpu, wl, I.sample_rows(wl, n_uniform=24))
 
 
