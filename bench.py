@@ -270,7 +270,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # MFMA operand type of the path: bf16 (attention, bf16 indexer) or fp8 e4m3 (indexer
+        # of an indexer-only workload); top-k is integer work on the fp32 scores.
+        "dtype": "fp8" if (wl.index_dtype == "fp8" and not has_attn) else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "n_tokens": n, "n_pools": p, "h_i": wl.h_i,
                    "d_i": wl.d_i, "index_dtype": wl.index_dtype, "topk": k,
