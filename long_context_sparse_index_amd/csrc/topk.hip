@@ -309,6 +309,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
       // The remaining 20 key bits over the candidates only.
       const int nc = static_cast<int>(in0);
       bool tied = false;
+      uint32_t n_tied = 0u;  // candidates on the final prefix (when tied: the exact key)
       for (int shift = 10; shift >= 0; shift -= 10) {
         for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
         __syncthreads();
@@ -323,14 +324,35 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
         prefix |= bin << shift;
         mask |= 0x3FFu << shift;
         krem -= static_cast<int>(above_bin);
+        n_tied = in_bin;
         tied = in_bin != static_cast<uint32_t>(krem);
         if (!tied) break;
       }
       // More candidates carry the threshold key than slots remain: the lowest pools among
-      // them win.  Pools are distinct, so a select on ~pool (larger = lower pool) over
-      // 10-bit windows at bits 22, 12, 2 and 0 ends with exactly krem of them.
+      // them win.  Up to one per thread, each tied candidate counts the tied pools below
+      // its own (pools are distinct, so these ranks are exact) and the one ranked krem - 1
+      // gives the largest winning pool.  More of them: a select on ~pool (larger = lower
+      // pool) over 10-bit windows at bits 22, 12, 2 and 0 ends with exactly krem of them.
       uint32_t pprefix = 0u, pmask = 0u;
-      if (tied) {
+      if (tied && n_tied <= static_cast<uint32_t>(kTopkThreads)) {
+        if (tid == 0) fill[1] = 0u;  // the candidate count is no longer needed
+        __syncthreads();
+        for (int i = tid; i < nc; i += kTopkThreads) {
+          const uint64_t c = cand[i];
+          if (static_cast<uint32_t>(c >> 32) == prefix)
+            hist[atomicAdd(&fill[1], 1u)] = static_cast<uint32_t>(c);  // < n_tied
+        }
+        __syncthreads();
+        if (tid < static_cast<int>(n_tied)) {
+          const uint32_t mine = hist[tid];
+          uint32_t rank = 0u;
+          for (int i = 0; i < static_cast<int>(n_tied); ++i) rank += hist[i] < mine ? 1u : 0u;
+          if (rank == static_cast<uint32_t>(krem - 1)) pick[0] = mine;
+        }
+        __syncthreads();
+        pmask = ~0u;
+        pprefix = ~pick[0];  // winners: pool <= that pool
+      } else if (tied) {
         for (int shift = 22;; shift = shift > 2 ? shift - 10 : 0) {
           for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
           __syncthreads();
