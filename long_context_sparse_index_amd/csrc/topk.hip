@@ -32,6 +32,7 @@ constexpr int kMaxK = 4096;
 constexpr int kBins0 = 4096;  // first digit: the top 12 bits of the key
 constexpr int kCand = 4096;   // candidate list: keys of the first digit's threshold bin
 constexpr int kLoads = 2;     // float4 loads in flight per thread while streaming a row
+constexpr int kSampleMinVis = 32768;  // rows at least this long take the sampled select
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t index) {
   return (static_cast<uint64_t>(~key) << 32) | index;  // ascending = key desc, index asc
@@ -117,7 +118,7 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int ls) {
 // only strides across waves go through LDS, alternating between buf and alt so that one
 // barrier per such stage suffices.
 template <int R>
-__device__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
+__device__ __forceinline__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
   constexpr int kLogR = R == 1 ? 0 : (R == 2 ? 1 : 2);
   constexpr int kN = kTopkThreads * R;
   static_assert(R == 1 || R == 2 || R == 4, "1, 2 or 4 keys per thread");
@@ -173,7 +174,7 @@ __device__ void bitonic_sort_regs(uint64_t* buf, uint64_t* alt) {
 
 // Sorts buf[0, n2) ascending, n2 a power of two <= kMaxK; buf[n2, max(n2, 1024)) must hold
 // ~0 (padding sorts last).  alt is scratch of the same size.
-__device__ void sort_keys(uint64_t* buf, uint64_t* alt, int n2) {
+__device__ __forceinline__ void sort_keys(uint64_t* buf, uint64_t* alt, int n2) {
   if (n2 <= kTopkThreads)
     bitonic_sort_regs<1>(buf, alt);
   else if (n2 <= 2 * kTopkThreads)
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
   static_assert(kBins0 * 4 <= kCand * 8, "first histogram fits the candidate list");
   __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
   __shared__ uint32_t pick[3];
-  __shared__ uint32_t fill[2];  // slots taken in buf and in cand
+  __shared__ uint32_t fill[3];  // slots taken in buf and in cand; sample size
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -269,135 +270,23 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     }
   };
 
-  // Pass A: the top 12 bits of every visible key.
-  for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
-  if (tid < 2) fill[tid] = 0u;
-  __syncthreads();
-  stream_row([&](int i4, const f32x4& v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * i4 + e < vis) atomicAdd(&hist0[float_order_key(v[e]) >> 20], 1u);
-  });
-  __syncthreads();
-  uint32_t above0, in0;
-  const uint32_t b0 = pick_bin(hist0, kBins0, static_cast<uint32_t>(k), wave_tmp, pick,
-                               &above0, &in0);
-  uint32_t prefix = b0 << 20, mask = 0xFFF00000u;
-  int krem = k - static_cast<int>(above0);
-  const bool whole = in0 == static_cast<uint32_t>(krem);
-
-  if (whole || in0 <= static_cast<uint32_t>(kCand)) {
-    // Pass B, in any order: keys above the bin (and the bin's own when it is taken whole)
-    // are winners; the bin's keys otherwise go to the candidate list.  The final sort
-    // orders the winners, so slots come from LDS counters.
-    stream_row([&](int i4, const f32x4& v) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
-        const uint32_t key = float_order_key(v[e]);
-        const uint32_t d = key >> 20;
-        if (static_cast<int>(i) < vis && d >= b0) {
-          if (d > b0 || whole)
-            buf[atomicAdd(&fill[0], 1u)] = composite(key, i);  // < above0 + in0 (whole) <= k
-          else
-            cand[atomicAdd(&fill[1], 1u)] = (static_cast<uint64_t>(key) << 32) | i;  // < in0
-        }
-      }
-    });
-    __syncthreads();
-    if (!whole) {
-      // The remaining 20 key bits over the candidates only.
-      const int nc = static_cast<int>(in0);
-      bool tied = false;
-      uint32_t n_tied = 0u;  // candidates on the final prefix (when tied: the exact key)
-      for (int shift = 10; shift >= 0; shift -= 10) {
-        for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-        __syncthreads();
-        for (int i = tid; i < nc; i += kTopkThreads) {
-          const uint32_t key = static_cast<uint32_t>(cand[i] >> 32);
-          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
-        }
-        __syncthreads();
-        uint32_t above_bin, in_bin;
-        const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
-                                      &above_bin, &in_bin);
-        prefix |= bin << shift;
-        mask |= 0x3FFu << shift;
-        krem -= static_cast<int>(above_bin);
-        n_tied = in_bin;
-        tied = in_bin != static_cast<uint32_t>(krem);
-        if (!tied) break;
-      }
-      // More candidates carry the threshold key than slots remain: the lowest pools among
-      // them win.  Up to one per thread, each tied candidate counts the tied pools below
-      // its own (pools are distinct, so these ranks are exact) and the one ranked krem - 1
-      // gives the largest winning pool.  More of them: a select on ~pool (larger = lower
-      // pool) over 10-bit windows at bits 22, 12, 2 and 0 ends with exactly krem of them.
-      uint32_t pprefix = 0u, pmask = 0u;
-      if (tied && n_tied <= static_cast<uint32_t>(kTopkThreads)) {
-        if (tid == 0) fill[1] = 0u;  // the candidate count is no longer needed
-        __syncthreads();
-        for (int i = tid; i < nc; i += kTopkThreads) {
-          const uint64_t c = cand[i];
-          if (static_cast<uint32_t>(c >> 32) == prefix)
-            hist[atomicAdd(&fill[1], 1u)] = static_cast<uint32_t>(c);  // < n_tied
-        }
-        __syncthreads();
-        if (tid < static_cast<int>(n_tied)) {
-          const uint32_t mine = hist[tid];
-          uint32_t rank = 0u;
-          for (int i = 0; i < static_cast<int>(n_tied); ++i) rank += hist[i] < mine ? 1u : 0u;
-          if (rank == static_cast<uint32_t>(krem - 1)) pick[0] = mine;
-        }
-        __syncthreads();
-        pmask = ~0u;
-        pprefix = ~pick[0];  // winners: pool <= that pool
-      } else if (tied) {
-        for (int shift = 22;; shift = shift > 2 ? shift - 10 : 0) {
-          for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-          __syncthreads();
-          for (int i = tid; i < nc; i += kTopkThreads) {
-            const uint64_t c = cand[i];
-            const uint32_t npool = ~static_cast<uint32_t>(c);
-            if (static_cast<uint32_t>(c >> 32) == prefix && (npool & pmask) == pprefix)
-              atomicAdd(&hist[(npool >> shift) & 0x3FFu], 1u);
-          }
-          __syncthreads();
-          uint32_t above_bin, in_bin;
-          const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp,
-                                        pick, &above_bin, &in_bin);
-          pprefix |= bin << shift;
-          pmask |= 0x3FFu << shift;
-          krem -= static_cast<int>(above_bin);
-          if (in_bin == static_cast<uint32_t>(krem) || shift == 0) break;
-        }
-      }
-      // Winners among the candidates: above the threshold prefix, or on it and (when tied)
-      // at or above the pool threshold.
-      for (int i = tid; i < nc; i += kTopkThreads) {
-        const uint64_t c = cand[i];
-        const uint32_t key = static_cast<uint32_t>(c >> 32);
-        const uint32_t pool = static_cast<uint32_t>(c);
-        const uint32_t mk = key & mask;
-        if (mk > prefix || (mk == prefix && (~pool & pmask) >= pprefix))
-          buf[atomicAdd(&fill[0], 1u)] = composite(key, pool);  // k winners in all
-      }
-    }
-  } else {
-    // The bin holds more keys than the candidate list: resolve the remaining bits over the
-    // row, then one ordered pass places the keys above the threshold and hands the krem
-    // slots left to the threshold-equal keys of lowest pool.
-    for (int shift = 10; shift >= 0; shift -= 10) {
+  // Exact resolution among the candidates cand[0, nc): the keys are known to hold every
+  // key of the row that can still be selected above the current prefix (mask, prefix),
+  // krem slots remain.  10-bit digit windows at `shift` and then shift - 10 ... 0 (a last
+  // window may overlap bits already fixed); a prefix held by more candidates than slots
+  // after all 32 bits is an exact tie, resolved by pool.  Winners (keys above the prefix,
+  // or on it and among the lowest pools) go to buf through fill[0].
+  auto resolve_candidates = [&](int nc, uint32_t prefix, uint32_t mask, int krem, int shift) {
+    bool tied = false;
+    uint32_t n_tied = 0u;  // candidates on the final prefix (when tied: the exact key)
+    for (;; shift = shift > 10 ? shift - 10 : (shift > 0 ? 0 : -1)) {
+      if (shift < 0) break;
       for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
       __syncthreads();
-      stream_row([&](int i4, const f32x4& v) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = float_order_key(v[e]);
-          if (4 * i4 + e < vis && (key & mask) == prefix)
-            atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
-        }
-      });
+      for (int i = tid; i < nc; i += kTopkThreads) {
+        const uint32_t key = static_cast<uint32_t>(cand[i] >> 32);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
+      }
       __syncthreads();
       uint32_t above_bin, in_bin;
       const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
@@ -405,57 +294,248 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
       prefix |= bin << shift;
       mask |= 0x3FFu << shift;
       krem -= static_cast<int>(above_bin);
-      if (in_bin == static_cast<uint32_t>(krem)) break;
+      n_tied = in_bin;
+      tied = in_bin != static_cast<uint32_t>(krem);
+      if (!tied) break;
     }
-    // Thread t takes the 16 consecutive keys [16 t, 16 t + 16) of each 16384-key group, so a
-    // block scan of the per-thread counts gives pool-ordered ranks.
-    constexpr int kU = 4;  // float4 per thread per group
-    const uint32_t n_gt = static_cast<uint32_t>(k - krem);
-    uint32_t run_gt = 0u, run_eq = 0u;
-    for (int base4 = 0; base4 < n4; base4 += kU * kTopkThreads) {
-      f32x4 cur[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i4 = base4 + kU * tid + u;
-        cur[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    // More candidates carry the threshold key than slots remain: the lowest pools among
+    // them win.  Up to one per thread, each tied candidate counts the tied pools below
+    // its own (pools are distinct, so these ranks are exact) and the one ranked krem - 1
+    // gives the largest winning pool.  More of them: a select on ~pool (larger = lower
+    // pool) over 10-bit windows at bits 22, 12, 2 and 0 ends with exactly krem of them.
+    uint32_t pprefix = 0u, pmask = 0u;
+    if (tied && n_tied <= static_cast<uint32_t>(kTopkThreads)) {
+      if (tid == 0) fill[1] = 0u;  // the candidate count is no longer needed
+      __syncthreads();
+      for (int i = tid; i < nc; i += kTopkThreads) {
+        const uint64_t c = cand[i];
+        if (static_cast<uint32_t>(c >> 32) == prefix)
+          hist[atomicAdd(&fill[1], 1u)] = static_cast<uint32_t>(c);  // < n_tied
       }
-      uint32_t cgt = 0u, ceq = 0u;
-      uint32_t flags = 0u;  // bit e: above, bit 16 + e: equal
+      __syncthreads();
+      if (tid < static_cast<int>(n_tied)) {
+        const uint32_t mine = hist[tid];
+        uint32_t rank = 0u;
+        for (int i = 0; i < static_cast<int>(n_tied); ++i) rank += hist[i] < mine ? 1u : 0u;
+        if (rank == static_cast<uint32_t>(krem - 1)) pick[0] = mine;
+      }
+      __syncthreads();
+      pmask = ~0u;
+      pprefix = ~pick[0];  // winners: pool <= that pool
+    } else if (tied) {
+      for (int pshift = 22;; pshift = pshift > 2 ? pshift - 10 : 0) {
+        for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+        __syncthreads();
+        for (int i = tid; i < nc; i += kTopkThreads) {
+          const uint64_t c = cand[i];
+          const uint32_t npool = ~static_cast<uint32_t>(c);
+          if (static_cast<uint32_t>(c >> 32) == prefix && (npool & pmask) == pprefix)
+            atomicAdd(&hist[(npool >> pshift) & 0x3FFu], 1u);
+        }
+        __syncthreads();
+        uint32_t above_bin, in_bin;
+        const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
+                                      &above_bin, &in_bin);
+        pprefix |= bin << pshift;
+        pmask |= 0x3FFu << pshift;
+        krem -= static_cast<int>(above_bin);
+        if (in_bin == static_cast<uint32_t>(krem) || pshift == 0) break;
+      }
+    }
+    // Winners among the candidates: above the prefix, or on it and (when tied) at or
+    // above the pool threshold.
+    for (int i = tid; i < nc; i += kTopkThreads) {
+      const uint64_t c = cand[i];
+      const uint32_t key = static_cast<uint32_t>(c >> 32);
+      const uint32_t pool = static_cast<uint32_t>(c);
+      const uint32_t mk = key & mask;
+      if (mk > prefix || (mk == prefix && (~pool & pmask) >= pprefix))
+        buf[atomicAdd(&fill[0], 1u)] = composite(key, pool);  // k winners in all
+    }
+  };
+
+  // Long rows: estimate the key ranked about 1.5 k from a 1/16 sample of the row, then
+  // one pass collects every key at or above the estimate into the candidate list.  When
+  // the list holds at least k and at most kCand keys it contains the k winners, which are
+  // then resolved from LDS alone: the row is read 1 1/16 times instead of twice.  Any
+  // other count (rare; heavy ties) falls back to the two-pass select below.
+  bool sampled = false;
+  if (vis >= kSampleMinVis && 3 * k <= 2 * kCand) {
+    if (tid < 3) fill[tid] = 0u;
+    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+    __syncthreads();
+    // The sample: 256-byte pieces (16 float4), one every 4 KB (256 float4) of the row.
+    auto stream_sample = [&](auto&& f) {
+      for (int c = tid >> 4; 256 * c < n4; c += kTopkThreads / 16) {
+        const int i4 = 256 * c + (tid & 15);
+        if (i4 < n4) f(i4, *reinterpret_cast<const f32x4*>(srow + 4 * i4));
+      }
+    };
+    uint32_t n_local = 0u;
+    stream_sample([&](int i4, const f32x4& v) {
 #pragma unroll
-      for (int e = 0; e < 4 * kU; ++e) {
-        const int i = 4 * (base4 + kU * tid) + e;
-        const uint32_t mk = float_order_key(cur[e >> 2][e & 3]) & mask;
-        if (i < vis) {
-          if (mk > prefix) {
-            flags |= 1u << e;
-            ++cgt;
-          } else if (mk == prefix) {
-            flags |= 1u << (16 + e);
-            ++ceq;
-          }
+      for (int e = 0; e < 4; ++e)
+        if (4 * i4 + e < vis) {
+          atomicAdd(&hist[float_order_key(v[e]) >> 22], 1u);
+          ++n_local;
+        }
+    });
+    if (n_local) atomicAdd(&fill[2], n_local);
+    __syncthreads();
+    const uint32_t n_sample = fill[2];
+    // Rank of the estimate in the sample: 1.5 k scaled to the sample (at least 1).
+    const int64_t target = k + k / 2;
+    uint32_t rank = static_cast<uint32_t>((target * n_sample + vis / 2) / vis);
+    rank = rank < 1u ? 1u : (rank > n_sample ? n_sample : rank);
+    uint32_t above1, in1;
+    const uint32_t bin1 = pick_bin(hist, 1024, rank, wave_tmp, pick, &above1, &in1);
+    const uint32_t prefix1 = bin1 << 22;
+    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+    __syncthreads();
+    stream_sample([&](int i4, const f32x4& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = float_order_key(v[e]);
+        if (4 * i4 + e < vis && (key & 0xFFC00000u) == prefix1)
+          atomicAdd(&hist[(key >> 12) & 0x3FFu], 1u);
+      }
+    });
+    __syncthreads();
+    uint32_t above2, in2;
+    const uint32_t bin2 = pick_bin(hist, 1024, rank - above1, wave_tmp, pick, &above2, &in2);
+    const uint32_t t_est = prefix1 | (bin2 << 12);  // lower edge of the estimate's 20-bit bin
+    stream_row([&](int i4, const f32x4& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
+        const uint32_t key = float_order_key(v[e]);
+        if (static_cast<int>(i) < vis && key >= t_est) {
+          const uint32_t slot = atomicAdd(&fill[1], 1u);
+          if (slot < static_cast<uint32_t>(kCand))
+            cand[slot] = (static_cast<uint64_t>(key) << 32) | i;
         }
       }
-      uint32_t tot;
-      const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
-      if (flags != 0u) {
-        uint32_t pos_gt = run_gt + (pre & 0xFFFFu);
-        uint32_t rank_eq = run_eq + (pre >> 16);
+    });
+    __syncthreads();
+    const uint32_t n_cand = fill[1];
+    sampled = n_cand >= static_cast<uint32_t>(k) && n_cand <= static_cast<uint32_t>(kCand);
+    __syncthreads();  // fill[] is reset below
+    if (sampled) resolve_candidates(static_cast<int>(n_cand), 0u, 0u, k, 22);
+  }
+
+  if (!sampled) {
+    // Pass A: the top 12 bits of every visible key.
+    for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
+    if (tid < 2) fill[tid] = 0u;
+    __syncthreads();
+    stream_row([&](int i4, const f32x4& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * i4 + e < vis) atomicAdd(&hist0[float_order_key(v[e]) >> 20], 1u);
+    });
+    __syncthreads();
+    uint32_t above0, in0;
+    const uint32_t b0 = pick_bin(hist0, kBins0, static_cast<uint32_t>(k), wave_tmp, pick,
+                                 &above0, &in0);
+    uint32_t prefix = b0 << 20, mask = 0xFFF00000u;
+    int krem = k - static_cast<int>(above0);
+    const bool whole = in0 == static_cast<uint32_t>(krem);
+
+    if (whole || in0 <= static_cast<uint32_t>(kCand)) {
+      // Pass B, in any order: keys above the bin (and the bin's own when it is taken whole)
+      // are winners; the bin's keys otherwise go to the candidate list.  The final sort
+      // orders the winners, so slots come from LDS counters.
+      stream_row([&](int i4, const f32x4& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
+          const uint32_t key = float_order_key(v[e]);
+          const uint32_t d = key >> 20;
+          if (static_cast<int>(i) < vis && d >= b0) {
+            if (d > b0 || whole)
+              buf[atomicAdd(&fill[0], 1u)] = composite(key, i);  // < above0 + in0 (whole) <= k
+            else
+              cand[atomicAdd(&fill[1], 1u)] = (static_cast<uint64_t>(key) << 32) | i;  // < in0
+          }
+        }
+      });
+      __syncthreads();
+      // The remaining 20 key bits over the bin's keys only (their winners join buf).
+      if (!whole) resolve_candidates(static_cast<int>(in0), prefix, mask, krem, 10);
+    } else {
+      // The bin holds more keys than the candidate list: resolve the remaining bits over the
+      // row, then one ordered pass places the keys above the threshold and hands the krem
+      // slots left to the threshold-equal keys of lowest pool.
+      for (int shift = 10; shift >= 0; shift -= 10) {
+        for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+        __syncthreads();
+        stream_row([&](int i4, const f32x4& v) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = float_order_key(v[e]);
+            if (4 * i4 + e < vis && (key & mask) == prefix)
+              atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
+          }
+        });
+        __syncthreads();
+        uint32_t above_bin, in_bin;
+        const uint32_t bin = pick_bin(hist, 1024, static_cast<uint32_t>(krem), wave_tmp, pick,
+                                      &above_bin, &in_bin);
+        prefix |= bin << shift;
+        mask |= 0x3FFu << shift;
+        krem -= static_cast<int>(above_bin);
+        if (in_bin == static_cast<uint32_t>(krem)) break;
+      }
+      // Thread t takes the 16 consecutive keys [16 t, 16 t + 16) of each 16384-key group, so a
+      // block scan of the per-thread counts gives pool-ordered ranks.
+      constexpr int kU = 4;  // float4 per thread per group
+      const uint32_t n_gt = static_cast<uint32_t>(k - krem);
+      uint32_t run_gt = 0u, run_eq = 0u;
+      for (int base4 = 0; base4 < n4; base4 += kU * kTopkThreads) {
+        f32x4 cur[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i4 = base4 + kU * tid + u;
+          cur[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        uint32_t cgt = 0u, ceq = 0u;
+        uint32_t flags = 0u;  // bit e: above, bit 16 + e: equal
 #pragma unroll
         for (int e = 0; e < 4 * kU; ++e) {
-          const uint32_t i = static_cast<uint32_t>(4 * (base4 + kU * tid) + e);
-          const uint32_t key = float_order_key(cur[e >> 2][e & 3]);
-          if (flags & (1u << e)) {
-            buf[pos_gt++] = composite(key, i);
-          } else if (flags & (1u << (16 + e))) {
-            if (rank_eq < static_cast<uint32_t>(krem)) buf[n_gt + rank_eq] = composite(key, i);
-            ++rank_eq;
+          const int i = 4 * (base4 + kU * tid) + e;
+          const uint32_t mk = float_order_key(cur[e >> 2][e & 3]) & mask;
+          if (i < vis) {
+            if (mk > prefix) {
+              flags |= 1u << e;
+              ++cgt;
+            } else if (mk == prefix) {
+              flags |= 1u << (16 + e);
+              ++ceq;
+            }
           }
         }
+        uint32_t tot;
+        const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
+        if (flags != 0u) {
+          uint32_t pos_gt = run_gt + (pre & 0xFFFFu);
+          uint32_t rank_eq = run_eq + (pre >> 16);
+#pragma unroll
+          for (int e = 0; e < 4 * kU; ++e) {
+            const uint32_t i = static_cast<uint32_t>(4 * (base4 + kU * tid) + e);
+            const uint32_t key = float_order_key(cur[e >> 2][e & 3]);
+            if (flags & (1u << e)) {
+              buf[pos_gt++] = composite(key, i);
+            } else if (flags & (1u << (16 + e))) {
+              if (rank_eq < static_cast<uint32_t>(krem)) buf[n_gt + rank_eq] = composite(key, i);
+              ++rank_eq;
+            }
+          }
+        }
+        run_gt += tot & 0xFFFFu;
+        run_eq += tot >> 16;
+        if (run_gt >= n_gt && run_eq >= static_cast<uint32_t>(krem)) break;  // uniform
       }
-      run_gt += tot & 0xFFFFu;
-      run_eq += tot >> 16;
-      if (run_gt >= n_gt && run_eq >= static_cast<uint32_t>(krem)) break;  // uniform
     }
   }
 

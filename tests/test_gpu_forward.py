@@ -143,6 +143,30 @@ def test_topk_pool_counts(gpu, p, kind, k):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("kind", ["sampled_high", "sampled_low"])
+def test_topk_long_rows_sample_fallbacks(gpu, kind):
+    """Long rows estimate their threshold from 256-byte pieces every 4 KB of the row (score
+    positions i with i % 1024 < 64).  Scores that make those pieces unrepresentative push
+    the candidate count below k (sampled_high) or past the candidate list (sampled_low);
+    either way the result must stay exact."""
+    say("case: topk long rows, %s" % kind)
+    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    p, k = 70000, 2048
+    rows = np.array([4 * 32768 - 1, 4 * 40000 + 3, 4 * p + 7], dtype=np.int64)
+    pos = np.arange(p)
+    in_sample = (pos % 1024) < 64
+    shift = 10.0 if kind == "sampled_high" else -10.0
+    host = np.stack([(rng.normal(size=p) + np.where(in_sample, shift, 0.0)).astype(np.float32)
+                     for _ in rows])
+    scores = torch.from_numpy(host).to(gpu)
+    idx = torch.empty((len(rows), k), dtype=torch.int32, device=gpu)
+    for r, t in enumerate(rows):
+        B.topk(scores[r:r + 1], idx[r:r + 1], q_start=int(t), n_pools=p)
+    torch.cuda.synchronize()
+    ref = oracle.topk(host, rows, p, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 def test_topk_chunk_of_consecutive_rows(gpu):
     say("case: topk consecutive rows, clustered ints, q_start=100000")
     rng = np.random.default_rng(5)
