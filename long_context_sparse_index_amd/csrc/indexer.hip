@@ -288,12 +288,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   }
 }
 
-template <int D, bool FP8>
-hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
-                            int64_t k_row_stride, const float* w, int64_t w_row_stride,
-                            float* scores, int64_t ld, int64_t q_start, int64_t nq,
-                            int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
-  constexpr int NB = 2;
+template <int D, int NB, bool FP8>
+hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
+                             int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                             float* scores, int64_t ld, int64_t q_start, int64_t nq,
+                             int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
   constexpr int kBQ = 16 * NB;
   const int64_t elt = FP8 ? 1 : 2;
   const int64_t vis_max = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
@@ -309,6 +308,25 @@ hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
                      w_row_stride, scores, ld, q_start, nq, n_pools, h_i, accumulate,
                      static_cast<int>(n_pool_tiles), static_cast<int>(n_query_tiles));
   return hipGetLastError();
+}
+
+// Query tile of 32 rows, or of 64 rows when few heads (at most 8) leave each block little
+// MFMA work per key-row load: the larger tile doubles the queries each key row serves
+// (measured 5% faster at 8 heads, 3% slower at 32).  The 64-row tile is kept to d_i <= 128,
+// whose key, score and product registers still fit.
+template <int D, bool FP8>
+hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
+                            int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                            float* scores, int64_t ld, int64_t q_start, int64_t nq,
+                            int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
+  if constexpr (D <= 128) {
+    if (h_i <= 8)
+      return launch_indexer_nb<D, 4, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
+                                          scores, ld, q_start, nq, n_pools, h_i, accumulate,
+                                          stream);
+  }
+  return launch_indexer_nb<D, 2, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride, scores,
+                                      ld, q_start, nq, n_pools, h_i, accumulate, stream);
 }
 
 }  // namespace

@@ -45,7 +45,9 @@ def test_indexer_tiny_full_bit_exact(gpu):
 @pytest.mark.parametrize("d_i", [32, 64, 128, 256])
 def test_indexer_ragged_offsets_negative_weights_accumulate(gpu, d_i):
     say("case: indexer ragged d_i=%d" % d_i)
-    nq, q_start, p, h_i, ld = 777, 1234, 301, 5, 304
+    # 12 heads, written as 3 then accumulated as 9: calls with at most 8 heads and with
+    # more take the two query-tile sizes of the kernel
+    nq, q_start, p, h_i, ld = 777, 1234, 301, 12, 304
     g = torch.Generator(device=gpu).manual_seed(7 + d_i)
     q = torch.randint(-4, 5, (nq, h_i, d_i), generator=g, device=gpu, dtype=torch.int8).to(
         torch.bfloat16)
@@ -54,7 +56,7 @@ def test_indexer_ragged_offsets_negative_weights_accumulate(gpu, d_i):
     choices = torch.tensor([1.0, 0.5, -0.25, 2.0, 0.0], device=gpu)
     w = choices[torch.randint(0, 5, (nq, h_i), generator=g, device=gpu)].float().contiguous()
     scores = torch.full((nq, ld), float("nan"), device=gpu)
-    # heads 0..2 written, heads 3..4 accumulated on top (a head-share partial sum)
+    # heads 0..2 written, heads 3..11 accumulated on top (a head-share partial sum)
     B.index_scores(q[:, :3], k, w[:, :3], scores, q_start=q_start)
     B.index_scores(q[:, 3:], k, w[:, 3:], scores, q_start=q_start, accumulate=True)
     torch.cuda.synchronize()
@@ -63,9 +65,10 @@ def test_indexer_ragged_offsets_negative_weights_accumulate(gpu, d_i):
     _check_scores(scores, ref, rows, p)
 
 
-def test_indexer_fp8_bit_exact(gpu):
-    say("case: indexer fp8 e4m3, d_i=128")
-    wl = W.Workload(name="fp8_small", n_tokens=3000, n_pools=750, h_i=6, d_i=128,
+@pytest.mark.parametrize("h_i", [6, 12])
+def test_indexer_fp8_bit_exact(gpu, h_i):
+    say("case: indexer fp8 e4m3, d_i=128, %d heads" % h_i)
+    wl = W.Workload(name="fp8_small", n_tokens=3000, n_pools=750, h_i=h_i, d_i=128,
                     index_dtype="fp8", int_range=8, w_period=4, topk=64)
     q, k, w = I.index_inputs(wl, gpu, seed=3)
     scores = B.index_scores_new(q, k, w)
