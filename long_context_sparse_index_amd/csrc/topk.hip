@@ -234,6 +234,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
   __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
   __shared__ uint32_t pick[3];
   __shared__ uint32_t fill[3];  // slots taken in buf and in cand; sample size
+  __shared__ uint32_t cand_max;  // largest key collected by the sampled path
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -362,14 +363,23 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
   bool sampled = false;
   if (vis >= kSampleMinVis && 3 * k <= 2 * kCand) {
     if (tid < 3) fill[tid] = 0u;
+    if (tid == 0) cand_max = 0u;
     for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
     __syncthreads();
-    // The sample: 256-byte pieces (16 float4), one every 4 KB (256 float4) of the row.
+    // The sample: 256-byte pieces (16 float4), one every 4 KB (256 float4) of the row, or
+    // sparser on rows past 2^18 keys so that there are at most 256 pieces: four per group
+    // of 16 threads, all loaded before any is used (one memory latency per sample pass).
+    const int piece_stride = 256 * ((n4 + 65535) / 65536);
     auto stream_sample = [&](auto&& f) {
-      for (int c = tid >> 4; 256 * c < n4; c += kTopkThreads / 16) {
-        const int i4 = 256 * c + (tid & 15);
-        if (i4 < n4) f(i4, *reinterpret_cast<const f32x4*>(srow + 4 * i4));
+      f32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i4 = piece_stride * ((tid >> 4) + 64 * j) + (tid & 15);
+        v[j] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f(piece_stride * ((tid >> 4) + 64 * j) + (tid & 15), v[j]);
     };
     uint32_t n_local = 0u;
     stream_sample([&](int i4, const f32x4& v) {
@@ -404,6 +414,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     uint32_t above2, in2;
     const uint32_t bin2 = pick_bin(hist, 1024, rank - above1, wave_tmp, pick, &above2, &in2);
     const uint32_t t_est = prefix1 | (bin2 << 12);  // lower edge of the estimate's 20-bit bin
+    uint32_t my_max = 0u;
     stream_row([&](int i4, const f32x4& v) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -413,14 +424,32 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
           const uint32_t slot = atomicAdd(&fill[1], 1u);
           if (slot < static_cast<uint32_t>(kCand))
             cand[slot] = (static_cast<uint64_t>(key) << 32) | i;
+          my_max = key > my_max ? key : my_max;
         }
       }
     });
+    if (my_max) atomicMax(&cand_max, my_max);
     __syncthreads();
     const uint32_t n_cand = fill[1];
     sampled = n_cand >= static_cast<uint32_t>(k) && n_cand <= static_cast<uint32_t>(kCand);
     __syncthreads();  // fill[] is reset below
-    if (sampled) resolve_candidates(static_cast<int>(n_cand), 0u, 0u, k, 22);
+    if (sampled) {
+      // The candidates lie in [t_est, cand_max]: the top bits those two share are fixed, and
+      // the select starts at the first 10-bit window where they differ.
+      const uint32_t diff = t_est ^ cand_max;
+      uint32_t prefix = 0u, mask = 0u;
+      int shift = 22;
+      if (diff < (1u << 22)) {
+        mask = 0xFFC00000u;
+        shift = 12;
+        if (diff < (1u << 12)) {
+          mask = 0xFFFFF000u;
+          shift = 2;
+        }
+        prefix = t_est & mask;
+      }
+      resolve_candidates(static_cast<int>(n_cand), prefix, mask, k, shift);
+    }
   }
 
   if (!sampled) {
