@@ -115,6 +115,32 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, int64_t q_start, int
 size_t dsa_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k);
 
 /*
+ * dsa_index_topk - dsa_index_scores followed by dsa_topk for rows [q_start, q_start + nq),
+ * with the same result (idx bit-identical to the two calls), usually without writing the
+ * score matrix.  Source: page "SkyRL ... 1 million tokens", section "Four optimizations",
+ * item 1 (indexer computed per query chunk, only int32 indices leave it); carrying the
+ * chunking down into the indexer's own tiles is this library's extension.
+ * Steps: scores of every 16th visible pool give each row a threshold about 1.5 k keys deep
+ * (rows with at most 4096 visible pools take every visible pool); the indexer then keeps,
+ * per row, only the (score, pool) pairs at or above the threshold; the top-k is resolved
+ * over those.  A row whose list does not hold between k and 4096 pairs (heavy ties at the
+ * threshold, adversarial score layouts) is redone exactly: the plain indexer writes the
+ * chunk's scores into the workspace and dsa_topk's select runs on that row.  Both redo
+ * launches are always enqueued and do nothing on the device when no row needs them.
+ *   Operands as dsa_index_scores (accumulate = 0) and dsa_topk.
+ *   ws: at least dsa_index_topk_workspace_bytes(nq, n_pools, k) bytes, 256-byte aligned
+ *   (candidate lists of 32 KB per row plus a full score buffer for the redo).
+ *   Supported: as dsa_index_scores; 1 <= k <= 2730 (DSA_ERR_UNSUPPORTED above: use the two
+ *   calls).
+ */
+dsa_status dsa_index_topk(const void* q_idx, int64_t q_row_stride, const void* k_idx,
+                          int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                          int64_t q_start, int64_t nq, int64_t n_pools, int32_t h_i,
+                          int32_t d_i, int32_t dtype, int32_t k, int32_t* idx, void* ws,
+                          size_t ws_bytes, void* stream);
+size_t dsa_index_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k);
+
+/*
  * dsa_sparse_attn_fwd - sparse MQA attention over the selected pooled KV rows.
  * Source: page "SkyRL ... 1 million tokens", section "Model and bottleneck" (attention
  * reads only the selected entries) and section "Four optimizations", item 1 (DeepSeek-V3.2
@@ -172,8 +198,9 @@ size_t dsa_sparse_attn_bwd_workspace_bytes(int64_t nq, int32_t h);
 
 /*
  * dsa_forward_chunked - the whole DSA forward over n_tokens queries, one query chunk at a
- * time: for each chunk [t0, t0 + chunk) it runs dsa_index_scores into one reused fp32
- * score buffer in the workspace, dsa_topk, and dsa_sparse_attn_fwd.  Source: page
+ * time: for each chunk [t0, t0 + chunk) it runs the select (dsa_index_topk when k <= 2730,
+ * else dsa_index_scores into one reused fp32 score buffer in the workspace and dsa_topk),
+ * then dsa_sparse_attn_fwd.  Source: page
  * "SkyRL ... 1 million tokens", section "Four optimizations", item 1 (indexer scores
  * computed in chunks per query, so the quadratic score matrix never exists beyond one
  * chunk).  Results do not depend on `chunk`.

@@ -58,6 +58,9 @@ _SIGNATURES = {
                              _I64, _I32, _I32, _I32, _F32, _I32, _I64, _I64, _I64, _P, _I32, _P,
                              _P, _P, _SZ, _P], ctypes.c_int),
     "dsa_forward_chunked_workspace_bytes": ([_I64, _I64, _I32], _SZ),
+    "dsa_index_topk": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+                        _P, _P, _SZ, _P], ctypes.c_int),
+    "dsa_index_topk_workspace_bytes": ([_I64, _I64, _I32], _SZ),
 }
 
 _lock = threading.Lock()
@@ -156,6 +159,32 @@ def topk(scores, idx, *, q_start: int, n_pools: int, ws=None, stream=None):
     _check(lib.dsa_topk(_ptr(scores), scores.stride(0), q_start, nq, n_pools, k, _ptr(idx),
                         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                         _stream(stream)))
+    return idx
+
+
+def index_topk_workspace_bytes(nq: int, n_pools: int, k: int) -> int:
+    return int(load_library().dsa_index_topk_workspace_bytes(nq, n_pools, k))
+
+
+def index_topk(q_idx, k_idx, w, idx, *, q_start: int = 0, n_pools: int | None = None, ws=None,
+               stream=None):
+    """idx[r, :] = top-k of the indexer scores of query q_start + r (fused select; the same
+    result as index_scores followed by topk)."""
+    nq, h_i, d_i = q_idx.shape
+    k = idx.shape[1]
+    n_pools = k_idx.shape[0] if n_pools is None else n_pools
+    assert q_idx.stride(2) == 1 and q_idx.stride(1) == d_i and k_idx.stride(1) == 1
+    assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.shape[0] == nq
+    assert w.dtype == torch.float32
+    w_stride = 0 if w.dim() == 1 else w.stride(0)
+    if ws is None:
+        ws = torch.empty(max(index_topk_workspace_bytes(nq, n_pools, k), 1), dtype=torch.uint8,
+                         device=q_idx.device)
+    lib = load_library()
+    _check(lib.dsa_index_topk(_ptr(q_idx), _row_stride(q_idx), _ptr(k_idx), k_idx.stride(0),
+                              _ptr(w), w_stride, q_start, nq, n_pools, h_i, d_i,
+                              _dtype_code(q_idx), k, _ptr(idx), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)))
     return idx
 
 

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -110,6 +111,102 @@ dsa_status check_attn_args(const void* q, const void* kv, int64_t ld_kv, const v
     DSA_REQUIRE(d_v <= d_qk, "attn: aliased V needs d_v <= d_qk");
   }
   return DSA_OK;
+}
+
+// Fused select (indexer -> top-k without a score matrix in the common case).  Workspace of
+// one chunk of `rows` queries, each part 256-byte aligned:
+//   sample  [rows, ld_s] fp32   scores of every 16th pool (threshold estimate)
+//   cand    [rows, cap]  u64    candidate lists (order key << 32 | pool)
+//   t_est, cnt, fail [rows] u32/u32/i32; any_fail (one i32)
+//   scores  [rows, ld]   fp32   full scores, written only for the exact fallback
+constexpr int kSampleShift = 4;
+// The chunked driver takes the fused select for chunks whose first row sees at least this
+// many pools; on shorter rows the score-row select is as fast (measured on MI355X: the
+// candidate top-k's fixed per-row work then outweighs the score traffic it saves).
+constexpr int64_t kFusedMinVisible = 49152;
+
+struct FusedLayout {
+  size_t sample, cand, t_est, cnt, fail, any, scores, total;
+  int64_t ld_s, ld;
+};
+
+FusedLayout fused_layout(int64_t rows, int64_t n_pools) {
+  FusedLayout L{};
+  const int64_t cols = (n_pools + (int64_t{1} << kSampleShift) - 1) >> kSampleShift;
+  L.ld_s = score_ld(cols);
+  L.ld = score_ld(n_pools);
+  const size_t r = static_cast<size_t>(rows);
+  size_t off = 0;
+  L.sample = off;
+  off += align256(r * L.ld_s * sizeof(float));
+  L.cand = off;
+  off += align256(r * dsa::topk_cand_cap() * sizeof(uint64_t));
+  L.t_est = off;
+  off += align256(r * sizeof(uint32_t));
+  L.cnt = off;
+  off += align256(r * sizeof(uint32_t));
+  L.fail = off;
+  off += align256(r * sizeof(int32_t));
+  L.any = off;
+  off += 256;
+  L.scores = off;
+  off += align256(r * L.ld * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// Indexer scores and top-k of rows [q_start, q_start + nq) through the fused select: sampled
+// scores -> per-row threshold -> indexer emitting candidates -> top-k over the candidates;
+// rows whose candidate list cannot give the exact answer are redone by the plain indexer and
+// score-row top-k, both gated on device flags (no host synchronisation).  ws holds
+// fused_layout(nq, n_pools).total bytes, 256-byte aligned.
+hipError_t run_fused_select(const void* q_idx, int64_t q_row_stride, const void* k_idx,
+                            int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                            int32_t h_i, int32_t d_i, int32_t dtype, int64_t q_start,
+                            int64_t nq, int64_t n_pools, int32_t k, int32_t* idx, char* ws,
+                            hipStream_t s) {
+  const FusedLayout L = fused_layout(nq, n_pools);
+  float* sample = reinterpret_cast<float*>(ws + L.sample);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+  uint32_t* t_est = reinterpret_cast<uint32_t*>(ws + L.t_est);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+  int32_t* fail = reinterpret_cast<int32_t*>(ws + L.fail);
+  int32_t* any = reinterpret_cast<int32_t*>(ws + L.any);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+
+  dsa::IndexerOpts sopt;
+  sopt.pool_shift = kSampleShift;
+  hipError_t e = dsa::launch_index_scores(q_idx, q_row_stride, k_idx, k_row_stride, w,
+                                          w_row_stride, sample, L.ld_s, q_start, nq, n_pools,
+                                          h_i, d_i, dtype, 0, s, sopt);
+  if (e != hipSuccess) return e;
+  e = dsa::launch_topk_threshold(sample, L.ld_s, q_start, nq, n_pools, kSampleShift, k, t_est,
+                                 cnt, any, s);
+  if (e != hipSuccess) return e;
+  dsa::IndexerOpts copt;
+  copt.t_est = t_est;
+  copt.cand_cnt = cnt;
+  copt.cand = cand;
+  copt.cand_cap = dsa::topk_cand_cap();
+  e = dsa::launch_index_scores(q_idx, q_row_stride, k_idx, k_row_stride, w, w_row_stride,
+                               nullptr, 0, q_start, nq, n_pools, h_i, d_i, dtype, 0, s, copt);
+  if (e != hipSuccess) return e;
+  dsa::TopkCand cs;
+  cs.cand = cand;
+  cs.cap = dsa::topk_cand_cap();
+  cs.cnt = cnt;
+  cs.t_est = t_est;
+  cs.fail = fail;
+  cs.any_fail = any;
+  e = dsa::launch_topk_from_cand(cs, q_start, nq, n_pools, k, idx, s);
+  if (e != hipSuccess) return e;
+  dsa::IndexerOpts gopt;
+  gopt.gate = any;
+  gopt.gate_rows = fail;
+  e = dsa::launch_index_scores(q_idx, q_row_stride, k_idx, k_row_stride, w, w_row_stride,
+                               scores, L.ld, q_start, nq, n_pools, h_i, d_i, dtype, 0, s, gopt);
+  if (e != hipSuccess) return e;
+  return dsa::launch_topk(scores, L.ld, q_start, nq, n_pools, k, idx, nullptr, 0, s, fail);
 }
 
 dsa_status check_out_dtype(int32_t o_dtype) {
@@ -224,11 +321,45 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, con
                     "dsa_sparse_attn_bwd launch");
 }
 
+size_t dsa_index_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k) {
+  if (nq <= 0 || k <= 0 || n_pools < 0) return 0;
+  return fused_layout(nq, n_pools).total;
+}
+
+dsa_status dsa_index_topk(const void* q_idx, int64_t q_row_stride, const void* k_idx,
+                          int64_t k_row_stride, const float* w, int64_t w_row_stride,
+                          int64_t q_start, int64_t nq, int64_t n_pools, int32_t h_i,
+                          int32_t d_i, int32_t dtype, int32_t k, int32_t* idx, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (dsa_status st = check_index_args(q_idx, q_row_stride, k_idx, k_row_stride, w,
+                                       w_row_stride, n_pools, h_i, d_i, dtype))
+    return st;
+  if (dsa_status st = check_topk_args(n_pools, k, idx)) return st;
+  DSA_REQUIRE(q_start >= 0 && nq >= 0, "index_topk: q_start and nq must be >= 0");
+  if (!dsa::topk_fused_supported(k))
+    return fail(DSA_ERR_UNSUPPORTED, "index_topk: k = %d > %d for the fused select", k,
+                2 * dsa::topk_cand_cap() / 3);
+  if (nq == 0) return ok();
+  const size_t need = dsa_index_topk_workspace_bytes(nq, n_pools, k);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(DSA_ERR_WORKSPACE,
+                "index_topk: 256-byte aligned workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : size_t{0});
+  return hip_status(run_fused_select(q_idx, q_row_stride, k_idx, k_row_stride, w,
+                                     w_row_stride, h_i, d_i, dtype, q_start, nq, n_pools, k,
+                                     idx, static_cast<char*>(ws),
+                                     static_cast<hipStream_t>(stream)),
+                    "dsa_index_topk launch");
+}
+
 size_t dsa_forward_chunked_workspace_bytes(int64_t n_pools, int64_t chunk, int32_t k) {
   if (chunk <= 0 || k <= 0 || n_pools < 0) return 0;
   const int64_t ld = score_ld(n_pools);
-  return align256(static_cast<size_t>(chunk) * ld * sizeof(float)) +
-         align256(static_cast<size_t>(chunk) * k * sizeof(int32_t)) +
+  const size_t idx_bytes = align256(static_cast<size_t>(chunk) * k * sizeof(int32_t));
+  if (dsa::topk_fused_supported(k))
+    return idx_bytes + fused_layout(chunk, n_pools).total +
+           align256(dsa::topk_workspace_bytes(chunk, n_pools, k));
+  return align256(static_cast<size_t>(chunk) * ld * sizeof(float)) + idx_bytes +
          align256(dsa::topk_workspace_bytes(chunk, n_pools, k));
 }
 
@@ -261,25 +392,37 @@ dsa_status dsa_forward_chunked(const void* q_idx, int64_t q_row_stride, const vo
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t ld = score_ld(n_pools);
+  const bool fused = dsa::topk_fused_supported(k);
   char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base);
-  int32_t* idx_ws =
-      reinterpret_cast<int32_t*>(base + align256(static_cast<size_t>(chunk) * ld * sizeof(float)));
-  char* topk_ws = reinterpret_cast<char*>(idx_ws) +
-                  align256(static_cast<size_t>(chunk) * k * sizeof(int32_t));
+  // Layout: idx chunk, then either the fused select's workspace (one chunk) or the score
+  // chunk and the top-k workspace.
+  int32_t* idx_ws = reinterpret_cast<int32_t*>(base);
+  char* rest = base + align256(static_cast<size_t>(chunk) * k * sizeof(int32_t));
+  // The score-row path uses the fused layout's score buffer when the fused select exists.
+  float* scores = reinterpret_cast<float*>(rest + (fused ? fused_layout(chunk, n_pools).scores : 0));
+  char* topk_ws = reinterpret_cast<char*>(scores) +
+                  align256(static_cast<size_t>(chunk) * ld * sizeof(float));
   const size_t topk_bytes = dsa::topk_workspace_bytes(chunk, n_pools, k);
   const int64_t ielt = idx_dtype == DSA_DTYPE_BF16 ? 2 : 1;
 
   for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
     const int64_t nq = (n_tokens - t0) < chunk ? (n_tokens - t0) : chunk;
-    hipError_t e = dsa::launch_index_scores(
-        static_cast<const char*>(q_idx) + t0 * q_row_stride * ielt, q_row_stride, k_idx,
-        k_row_stride, w + t0 * w_row_stride, w_row_stride, scores, ld, t0, nq, n_pools, h_i,
-        d_i, idx_dtype, 0, s);
-    if (e != hipSuccess) return hip_status(e, "dsa_forward_chunked: indexer launch");
+    const void* q_idx_c = static_cast<const char*>(q_idx) + t0 * q_row_stride * ielt;
     int32_t* idx_chunk = idx_out ? idx_out + t0 * k : idx_ws;
-    e = dsa::launch_topk(scores, ld, t0, nq, n_pools, k, idx_chunk, topk_ws, topk_bytes, s);
-    if (e != hipSuccess) return hip_status(e, "dsa_forward_chunked: top-k launch");
+    hipError_t e;
+    if (fused && std::min<int64_t>(n_pools, (t0 + 1) / 4) >= kFusedMinVisible) {
+      e = run_fused_select(q_idx_c, q_row_stride, k_idx, k_row_stride, w + t0 * w_row_stride,
+                           w_row_stride, h_i, d_i, idx_dtype, t0, nq, n_pools, k, idx_chunk,
+                           rest, s);
+      if (e != hipSuccess) return hip_status(e, "dsa_forward_chunked: select launch");
+    } else {
+      e = dsa::launch_index_scores(q_idx_c, q_row_stride, k_idx, k_row_stride,
+                                   w + t0 * w_row_stride, w_row_stride, scores, ld, t0, nq,
+                                   n_pools, h_i, d_i, idx_dtype, 0, s);
+      if (e != hipSuccess) return hip_status(e, "dsa_forward_chunked: indexer launch");
+      e = dsa::launch_topk(scores, ld, t0, nq, n_pools, k, idx_chunk, topk_ws, topk_bytes, s);
+      if (e != hipSuccess) return hip_status(e, "dsa_forward_chunked: top-k launch");
+    }
     const size_t o_elt = o_dtype == DSA_DTYPE_F32 ? 4 : 2;
     e = dsa::launch_sparse_attn_fwd(static_cast<const uint16_t*>(q) + t0 * h * d_qk, kv, ld_kv,
                                     v, ld_v, idx_chunk, k,

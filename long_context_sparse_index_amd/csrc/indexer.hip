@@ -97,13 +97,15 @@ __device__ __forceinline__ void idx_dma_16b(const void* src, uint32_t lds_addr) 
 // Waits until at most `n` vector-memory operations of this wave are outstanding (n < 64).
 #define IDX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
-// D: d_i; NB: 16-query column blocks per tile (BQ = 16 * NB); FP8: e4m3 operands.
-template <int D, int NB, bool FP8>
+// D: d_i; NB: 16-query column blocks per tile (BQ = 16 * NB); FP8: e4m3 operands; EMIT:
+// instead of storing scores, append the (key, pool) pairs whose order key reaches the row's
+// threshold to the row's candidate list (IndexerOpts).
+template <int D, int NB, bool FP8, bool EMIT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const uint8_t* __restrict__ q, int64_t q_stride_b, const uint8_t* __restrict__ k,
     int64_t k_stride_b, const float* __restrict__ w, int64_t w_stride,
     float* __restrict__ scores, int64_t ld, int64_t q_start, int64_t nq, int64_t n_pools,
-    int h_i, int accumulate, int n_pool_tiles, int n_query_tiles) {
+    int h_i, int accumulate, int n_pool_tiles, int n_query_tiles, IndexerOpts opt) {
   using Frag = typename FragT<FP8>::type;
   constexpr int kRowBytes = D * (FP8 ? 1 : 2);
   constexpr int kFragBytes = FP8 ? 32 : 16;        // bytes of one row per lane group
@@ -132,6 +134,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     else return (r / (16 / kCpr)) & (kCpr - 1);
   };
 
+  if (opt.gate && *opt.gate == 0) return;  // gated launch with nothing to do
+  // With pool_shift s the key table is read at every 2^s-th pool (the caller scales the key
+  // stride): column c is pool c * 2^s, visible to t iff c * 2^s < V(t).
+  const int sh = opt.pool_shift;
+  auto vis_of = [&](int64_t t) {
+    return (visible_pools(t, n_pools) + (int64_t{1} << sh) - 1) >> sh;
+  };
+  const int64_t n_cols = (n_pools + (int64_t{1} << sh) - 1) >> sh;
   // XCD-aware remap: consecutive logical tiles (same query tile) land on one XCD.
   const int n_tiles = n_pool_tiles * n_query_tiles;
   const int per_xcd = (n_tiles + 7) >> 3;
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int64_t q0 = static_cast<int64_t>(qt) * kBQ;
   const int64_t p0 = static_cast<int64_t>(pt) * kPoolsPerBlock;
   const int64_t rows_here = (nq - q0) < kBQ ? (nq - q0) : kBQ;
-  const int64_t vis_last = visible_pools(q_start + q0 + rows_here - 1, n_pools);
+  const int64_t vis_last = vis_of(q_start + q0 + rows_here - 1);
   if (p0 >= vis_last) return;  // whole tile above the causal boundary
 
   const int tid = threadIdx.x;
@@ -152,6 +162,22 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int r16 = lane & 15;
   const int64_t pw0 = p0 + wid * kPoolsPerWave;
   const bool wave_live = pw0 < vis_last;
+
+  if (opt.gate_rows) {
+    // Only query tiles holding a flagged row: wave 0 checks the tile's rows (kBQ <= 64) and
+    // passes the verdict through the weight array's first word before the weights land.
+    static_assert(kBQ <= kWave, "one wave checks the tile");
+    uint32_t* const verdict = reinterpret_cast<uint32_t*>(w_lds);
+    if (tid < kWave) {
+      const bool flagged = tid < kBQ && q0 + tid < nq && opt.gate_rows[q0 + tid] != 0;
+      const uint64_t b = __ballot(flagged);
+      if (tid == 0) *verdict = b != 0 ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool any_row = *verdict != 0u;
+    __syncthreads();  // the weights overwrite the verdict next
+    if (!any_row) return;
+  }
 
   // Head weights of the tile's queries, stored [head][query] so that the 16 lanes of a group
   // read 16 consecutive words.
@@ -166,7 +192,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
     const int64_t pool = pw0 + mb * 16 + r16;
-    const bool ok = wave_live && pool < n_pools;
+    const bool ok = wave_live && pool < n_cols;
     const uint8_t* kp = k + (ok ? pool : 0) * k_stride_b + g * kFragBytes;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
@@ -263,13 +289,76 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       }
     }
   }
+  if constexpr (EMIT) {
+    // Candidates: visible entries whose order key reaches the row's threshold, i.e. whose
+    // score is >= the threshold's float (one compare each; a threshold key of 0 takes every
+    // finite score).  Each lane marks its candidates in a bit mask per row, takes its offset
+    // in the tile's share of the row with one LDS atomic, one thread per row reserves that
+    // share in the row's list, and the marked entries are written.  The counters reuse the
+    // head weights' LDS once every wave is past the loop.
+    static_assert(2 * kBQ <= kBQ * kMaxHeads, "counters fit the weight array");
+    static_assert(kMB * 4 <= 32, "one 32-bit mask per row");
+    uint32_t* const c_cnt = reinterpret_cast<uint32_t*>(w_lds);
+    uint32_t* const c_base = c_cnt + kBQ;
+    __syncthreads();
+    if (tid < kBQ) c_cnt[tid] = 0u;
+    __syncthreads();
+    uint32_t mask[NB], off[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t row = q0 + nb * 16 + r16;
+      const bool live = wave_live && row < nq;
+      const int64_t vis = live ? vis_of(q_start + row) : 0;
+      const uint32_t tk = live ? opt.t_est[row] : 0u;
+      // float at the lower edge of the threshold key (keys with the top bit set are the
+      // non-negative floats)
+      const float thr = tk == 0u ? -__builtin_inff()
+                                 : __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
+      uint32_t m = 0u;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t p = pw0 + mb * 16 + g * 4 + i;
+          m |= (p < vis && sc[mb][nb][i] >= thr) ? (1u << (mb * 4 + i)) : 0u;
+        }
+      mask[nb] = m;
+      off[nb] = m ? atomicAdd(&c_cnt[nb * 16 + r16], static_cast<uint32_t>(__builtin_popcount(m)))
+                  : 0u;
+    }
+    __syncthreads();
+    if (tid < kBQ && q0 + tid < nq) {
+      const uint32_t c = c_cnt[tid];
+      c_base[tid] = c ? atomicAdd(&opt.cand_cnt[q0 + tid], c) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (!mask[nb]) continue;
+      const int64_t row = q0 + nb * 16 + r16;
+      uint32_t slot = c_base[nb * 16 + r16] + off[nb];
+      uint64_t* const dst = opt.cand + row * opt.cand_cap;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (mask[nb] & (1u << (mb * 4 + i))) {
+            if (slot < static_cast<uint32_t>(opt.cand_cap))
+              dst[slot] = (static_cast<uint64_t>(float_order_key(sc[mb][nb][i])) << 32) |
+                          static_cast<uint32_t>(pw0 + mb * 16 + g * 4 + i);
+            ++slot;
+          }
+        }
+    }
+    return;
+  }
   if (!wave_live) return;
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int64_t row = q0 + nb * 16 + r16;
     if (row >= nq) continue;
-    const int64_t vis = visible_pools(q_start + row, n_pools);
+    const int64_t vis = vis_of(q_start + row);
     float* dst_row = scores + row * ld;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
@@ -292,21 +381,25 @@ template <int D, int NB, bool FP8>
 hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
                              int64_t k_row_stride, const float* w, int64_t w_row_stride,
                              float* scores, int64_t ld, int64_t q_start, int64_t nq,
-                             int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
+                             int64_t n_pools, int h_i, int accumulate, const IndexerOpts& opt,
+                             hipStream_t stream) {
   constexpr int kBQ = 16 * NB;
   const int64_t elt = FP8 ? 1 : 2;
-  const int64_t vis_max = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
+  const int64_t step = int64_t{1} << opt.pool_shift;
+  const int64_t vis_pools = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
+  const int64_t vis_max = (vis_pools + step - 1) / step;
   if (nq <= 0 || vis_max <= 0) return hipSuccess;
   const int64_t n_query_tiles = (nq + kBQ - 1) / kBQ;
   const int64_t n_pool_tiles = (vis_max + kPoolsPerBlock - 1) / kPoolsPerBlock;
   const int64_t n_tiles = n_query_tiles * n_pool_tiles;
   if (n_tiles >= (int64_t{1} << 31) - 8) return hipErrorInvalidConfiguration;
   const int64_t grid = ((n_tiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((indexer_kernel<D, NB, FP8>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kIdxThreads), 0, stream, static_cast<const uint8_t*>(q),
-                     q_row_stride * elt, static_cast<const uint8_t*>(k), k_row_stride * elt, w,
+  auto kern = opt.cand ? indexer_kernel<D, NB, FP8, true> : indexer_kernel<D, NB, FP8, false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kIdxThreads), 0, stream,
+                     static_cast<const uint8_t*>(q), q_row_stride * elt,
+                     static_cast<const uint8_t*>(k), k_row_stride * elt * step, w,
                      w_row_stride, scores, ld, q_start, nq, n_pools, h_i, accumulate,
-                     static_cast<int>(n_pool_tiles), static_cast<int>(n_query_tiles));
+                     static_cast<int>(n_pool_tiles), static_cast<int>(n_query_tiles), opt);
   return hipGetLastError();
 }
 
@@ -318,15 +411,16 @@ template <int D, bool FP8>
 hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
                             int64_t k_row_stride, const float* w, int64_t w_row_stride,
                             float* scores, int64_t ld, int64_t q_start, int64_t nq,
-                            int64_t n_pools, int h_i, int accumulate, hipStream_t stream) {
+                            int64_t n_pools, int h_i, int accumulate, const IndexerOpts& opt,
+                            hipStream_t stream) {
   if constexpr (D <= 128) {
     if (h_i <= 8)
       return launch_indexer_nb<D, 4, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
                                           scores, ld, q_start, nq, n_pools, h_i, accumulate,
-                                          stream);
+                                          opt, stream);
   }
   return launch_indexer_nb<D, 2, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride, scores,
-                                      ld, q_start, nq, n_pools, h_i, accumulate, stream);
+                                      ld, q_start, nq, n_pools, h_i, accumulate, opt, stream);
 }
 
 }  // namespace
@@ -343,10 +437,11 @@ hipError_t launch_index_scores(const void* q, int64_t q_row_stride, const void* 
                                int64_t k_row_stride, const float* w, int64_t w_row_stride,
                                float* scores, int64_t ld, int64_t q_start, int64_t nq,
                                int64_t n_pools, int h_i, int d_i, int dtype, int accumulate,
-                               hipStream_t stream) {
+                               hipStream_t stream, const IndexerOpts& opt) {
+  if (opt.pool_shift < 0 || opt.pool_shift > 8) return hipErrorInvalidValue;
 #define DSA_IDX_CASE(DD, F8)                                                                 \
   return launch_indexer_t<DD, F8>(q, q_row_stride, k, k_row_stride, w, w_row_stride, scores, \
-                                  ld, q_start, nq, n_pools, h_i, accumulate, stream)
+                                  ld, q_start, nq, n_pools, h_i, accumulate, opt, stream)
   if (dtype == 0) {
     switch (d_i) {
       case 32: DSA_IDX_CASE(32, false);

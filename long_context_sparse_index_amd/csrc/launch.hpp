@@ -7,19 +7,57 @@
 
 namespace dsa {
 
+// Optional behaviour of the indexer launch.  pool_shift s: score only every 2^s-th pool
+// (column c of the output is pool c * 2^s).  gate: when non-null, the launch does nothing
+// unless *gate != 0 (read on the device); gate_rows (non-null): only query tiles that hold
+// a row r with gate_rows[r] != 0 are computed.  cand (non-null): instead of writing scores,
+// append (order key << 32 | pool) of every visible entry whose order key is >= t_est[row] to
+// cand[row * cand_cap + slot], slots taken from cand_cnt[row] (the caller zeroes it; a count
+// past cand_cap means entries were dropped).
+struct IndexerOpts {
+  int pool_shift = 0;
+  const int32_t* gate = nullptr;
+  const int32_t* gate_rows = nullptr;
+  const uint32_t* t_est = nullptr;
+  uint32_t* cand_cnt = nullptr;
+  uint64_t* cand = nullptr;
+  int cand_cap = 0;
+};
+
 bool indexer_supported(int d_i, int dtype);
 int indexer_max_heads();
 hipError_t launch_index_scores(const void* q, int64_t q_row_stride, const void* k,
                                int64_t k_row_stride, const float* w, int64_t w_row_stride,
                                float* scores, int64_t ld, int64_t q_start, int64_t nq,
                                int64_t n_pools, int h_i, int d_i, int dtype, int accumulate,
-                               hipStream_t stream);
+                               hipStream_t stream, const IndexerOpts& opt = IndexerOpts());
 
 int topk_max_k();
 size_t topk_workspace_bytes(int64_t nq, int64_t n_pools, int k);
+// gate (non-null): rows r with gate[r] == 0 are skipped (their idx rows are left as they are).
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t q_start, int64_t nq,
                        int64_t n_pools, int k, int32_t* idx, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+                       hipStream_t stream, const int32_t* gate = nullptr);
+
+// Fused select (indexer candidates -> top-k).  Candidate lists: cand[row * cap + slot] =
+// (order key << 32) | pool, cnt[row] entries written by the indexer (more than cap means
+// some were dropped).  fail[row] is set to 1 (and *any_fail to 1) for rows whose list cannot
+// give the exact result; 0 otherwise.
+struct TopkCand {
+  const uint64_t* cand = nullptr;
+  int cap = 0;
+  const uint32_t* cnt = nullptr;
+  const uint32_t* t_est = nullptr;
+  int32_t* fail = nullptr;
+  int32_t* any_fail = nullptr;
+};
+int topk_cand_cap();
+bool topk_fused_supported(int k);
+hipError_t launch_topk_threshold(const float* sample, int64_t ld_sample, int64_t q_start,
+                                 int64_t nq, int64_t n_pools, int shift, int k, uint32_t* t_est,
+                                 uint32_t* cnt, int32_t* any_fail, hipStream_t stream);
+hipError_t launch_topk_from_cand(const TopkCand& cs, int64_t q_start, int64_t nq,
+                                 int64_t n_pools, int k, int32_t* idx, hipStream_t stream);
 
 bool attn_shape_supported(int d_qk, int d_v);
 int attn_max_k();

@@ -221,10 +221,16 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, int nbins, ui
   return bin;
 }
 
+// FROM_CAND: the row's candidates come from a list written by the indexer (TopkCand)
+// instead of a score row; the row is flagged for the exact fallback when the list does not
+// hold between k and kCand entries.  Otherwise a non-null gate skips rows whose gate is 0.
+template <bool FROM_CAND>
 __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_kernel(const float* __restrict__ scores,
                                                             int64_t ld, int64_t q_start,
                                                             int64_t n_pools, int k,
-                                                            int32_t* __restrict__ idx) {
+                                                            int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ gate,
+                                                            TopkCand cs) {
   // The first-digit histogram is dead before the candidate list is written: they share LDS.
   __shared__ uint64_t cand[kCand];  // (key << 32) | pool
   __shared__ uint32_t hist[1024];   // 10-bit digit histograms
@@ -238,38 +244,11 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
+  if (!FROM_CAND && gate && gate[r] == 0) return;
   const int64_t vis64 = visible_pools(q_start + r, n_pools);
   const int vis = static_cast<int>(vis64);
   const float* srow = scores + r * ld;
   int32_t* orow = idx + r * k;
-
-  if (vis <= k) {
-    const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
-    for (int i = tid; i < n2; i += kTopkThreads)
-      buf[i] = i < vis ? composite(float_order_key(srow[i]), static_cast<uint32_t>(i)) : ~0ull;
-    __syncthreads();
-    sort_keys(buf, cand, n2);
-    for (int i = tid; i < k; i += kTopkThreads)
-      orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
-    return;
-  }
-
-  const int n4 = (vis + 3) >> 2;  // float4 groups; the row is padded to ld (a multiple of 4)
-  // Calls f(i4, v) for every float4 group of the row, kLoads loads in flight per thread.
-  // Groups past the row end carry keys with index >= vis, which f must skip.
-  auto stream_row = [&](auto&& f) {
-    for (int base = 0; base < n4; base += kLoads * kTopkThreads) {
-      f32x4 v[kLoads];
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int i4 = base + u * kTopkThreads + tid;
-        v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) f(base + u * kTopkThreads + tid, v[u]);
-    }
-  };
 
   // Exact resolution among the candidates cand[0, nc): the keys are known to hold every
   // key of the row that can still be selected above the current prefix (mask, prefix),
@@ -352,6 +331,100 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
       const uint32_t mk = key & mask;
       if (mk > prefix || (mk == prefix && (~pool & pmask) >= pprefix))
         buf[atomicAdd(&fill[0], 1u)] = composite(key, pool);  // k winners in all
+    }
+  };
+
+  if constexpr (FROM_CAND) {
+    // The list holds every visible entry whose key is >= the row's threshold (all visible
+    // entries when the threshold is 0).  With at least k (or all vis <= k) and at most kCand
+    // of them it holds the k winners, resolved here as in the sampled path; any other count
+    // leaves the row to the fallback (indexer scores + the score-row select).
+    const uint32_t n = cs.cnt[r];
+    const bool usable = vis <= k ? n == static_cast<uint32_t>(vis)
+                                 : (n >= static_cast<uint32_t>(k) &&
+                                    n <= static_cast<uint32_t>(kCand));
+    if (tid == 0) {
+      cs.fail[r] = usable ? 0 : 1;
+      if (!usable) atomicOr(cs.any_fail, 1);
+    }
+    if (!usable) return;
+    const uint64_t* crow = cs.cand + r * cs.cap;
+    if (vis <= k) {
+      const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
+      for (int i = tid; i < n2; i += kTopkThreads) {
+        if (i < vis) {
+          const uint64_t c = crow[i];
+          buf[i] = composite(static_cast<uint32_t>(c >> 32), static_cast<uint32_t>(c));
+        } else {
+          buf[i] = ~0ull;
+        }
+      }
+      __syncthreads();
+      sort_keys(buf, cand, n2);
+      for (int i = tid; i < k; i += kTopkThreads)
+        orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
+      return;
+    }
+    if (tid < 3) fill[tid] = 0u;
+    if (tid == 0) cand_max = 0u;
+    __syncthreads();
+    uint32_t my_max = 0u;
+    for (int i = tid; i < static_cast<int>(n); i += kTopkThreads) {
+      const uint64_t c = crow[i];
+      cand[i] = c;
+      const uint32_t key = static_cast<uint32_t>(c >> 32);
+      my_max = key > my_max ? key : my_max;
+    }
+    if (my_max) atomicMax(&cand_max, my_max);
+    __syncthreads();
+    const uint32_t t_est = cs.t_est[r];
+    const uint32_t diff = t_est ^ cand_max;
+    uint32_t prefix = 0u, mask = 0u;
+    int shift = 22;
+    if (diff < (1u << 22)) {
+      mask = 0xFFC00000u;
+      shift = 12;
+      if (diff < (1u << 12)) {
+        mask = 0xFFFFF000u;
+        shift = 2;
+      }
+      prefix = t_est & mask;
+    }
+    resolve_candidates(static_cast<int>(n), prefix, mask, k, shift);
+    const int n2 = max(next_pow2(k), kTopkThreads);
+    for (int i = k + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
+    __syncthreads();
+    sort_keys(buf, cand, n2);
+    for (int i = tid; i < k; i += kTopkThreads)
+      orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
+    return;
+  }
+
+  if (vis <= k) {
+    const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
+    for (int i = tid; i < n2; i += kTopkThreads)
+      buf[i] = i < vis ? composite(float_order_key(srow[i]), static_cast<uint32_t>(i)) : ~0ull;
+    __syncthreads();
+    sort_keys(buf, cand, n2);
+    for (int i = tid; i < k; i += kTopkThreads)
+      orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
+    return;
+  }
+
+  const int n4 = (vis + 3) >> 2;  // float4 groups; the row is padded to ld (a multiple of 4)
+  // Calls f(i4, v) for every float4 group of the row, kLoads loads in flight per thread.
+  // Groups past the row end carry keys with index >= vis, which f must skip.
+  auto stream_row = [&](auto&& f) {
+    for (int base = 0; base < n4; base += kLoads * kTopkThreads) {
+      f32x4 v[kLoads];
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int i4 = base + u * kTopkThreads + tid;
+        v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) f(base + u * kTopkThreads + tid, v[u]);
     }
   };
 
@@ -576,19 +649,97 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
 }
 
+// Per-row threshold for the fused select, from the scores of every 2^shift-th visible pool
+// (sample row of vs = ceil(V / 2^shift) entries): the lower edge of the 22-bit key bin that
+// holds the sample key ranked 1.5 k * vs / V, so that about 1.5 k keys of the full row reach
+// it.  Rows with at most kCand visible pools get threshold 0 (every visible key).  Also
+// zeroes the row's candidate count, and block 0 the any-fallback flag.
+__global__ __launch_bounds__(kTopkThreads) void threshold_kernel(
+    const float* __restrict__ sample, int64_t ld_sample, int64_t q_start, int64_t n_pools,
+    int shift, int k, uint32_t* __restrict__ t_est, uint32_t* __restrict__ cnt,
+    int32_t* __restrict__ any_fail) {
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
+  __shared__ uint32_t pick[3];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  if (tid == 0) {
+    cnt[r] = 0u;
+    if (r == 0) *any_fail = 0;
+  }
+  const int64_t vis = visible_pools(q_start + r, n_pools);
+  if (vis <= kCand) {
+    if (tid == 0) t_est[r] = 0u;
+    return;
+  }
+  const int vs = static_cast<int>((vis + (int64_t{1} << shift) - 1) >> shift);
+  const int vs4 = (vs + 3) >> 2;
+  const float* srow = sample + r * ld_sample;
+  const int64_t target = k + k / 2;
+  uint32_t rank = static_cast<uint32_t>((target * vs + vis / 2) / vis);
+  rank = rank < 1u ? 1u : (rank > static_cast<uint32_t>(vs) ? static_cast<uint32_t>(vs) : rank);
+  for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+  __syncthreads();
+  auto each_key = [&](auto&& f) {
+    for (int i4 = tid; i4 < vs4; i4 += kTopkThreads) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(srow + 4 * i4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * i4 + e < vs) f(float_order_key(v[e]));
+    }
+  };
+  each_key([&](uint32_t key) { atomicAdd(&hist[key >> 22], 1u); });
+  __syncthreads();
+  uint32_t above1, in1;
+  const uint32_t bin1 = pick_bin(hist, 1024, rank, wave_tmp, pick, &above1, &in1);
+  for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+  __syncthreads();
+  each_key([&](uint32_t key) {
+    if ((key >> 22) == bin1) atomicAdd(&hist[(key >> 12) & 0x3FFu], 1u);
+  });
+  __syncthreads();
+  uint32_t above2, in2;
+  const uint32_t bin2 = pick_bin(hist, 1024, rank - above1, wave_tmp, pick, &above2, &in2);
+  if (tid == 0) t_est[r] = (bin1 << 22) | (bin2 << 12);
+}
+
 }  // namespace
 
 int topk_max_k() { return kMaxK; }
+
+int topk_cand_cap() { return kCand; }
+
+bool topk_fused_supported(int k) { return k >= 1 && 3 * k <= 2 * kCand; }
 
 size_t topk_workspace_bytes(int64_t, int64_t, int) { return 0; }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t q_start, int64_t nq,
                        int64_t n_pools, int k, int32_t* idx, void*, size_t,
-                       hipStream_t stream) {
+                       hipStream_t stream, const int32_t* gate) {
   if (nq <= 0) return hipSuccess;
   if (nq >= (int64_t{1} << 31)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
-                     stream, scores, ld, q_start, n_pools, k, idx);
+  hipLaunchKernelGGL(topk_kernel<false>, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
+                     stream, scores, ld, q_start, n_pools, k, idx, gate, TopkCand());
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_threshold(const float* sample, int64_t ld_sample, int64_t q_start,
+                                 int64_t nq, int64_t n_pools, int shift, int k, uint32_t* t_est,
+                                 uint32_t* cnt, int32_t* any_fail, hipStream_t stream) {
+  if (nq <= 0) return hipSuccess;
+  if (nq >= (int64_t{1} << 31) || ld_sample % 4 != 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(threshold_kernel, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
+                     stream, sample, ld_sample, q_start, n_pools, shift, k, t_est, cnt, any_fail);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_from_cand(const TopkCand& cs, int64_t q_start, int64_t nq,
+                                 int64_t n_pools, int k, int32_t* idx, hipStream_t stream) {
+  if (nq <= 0) return hipSuccess;
+  if (nq >= (int64_t{1} << 31) || cs.cap < kCand || !topk_fused_supported(k))
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(topk_kernel<true>, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
+                     stream, nullptr, int64_t{0}, q_start, n_pools, k, idx, nullptr, cs);
   return hipGetLastError();
 }
 

@@ -1,0 +1,165 @@
+"""GPU parity of the fused select (dsa_index_topk): the indices must be bit-identical to
+dsa_index_scores followed by dsa_topk, and to the CPU oracle, on every path of the fused
+select: rows taking every visible pool, sampled thresholds, and rows redone exactly because
+their candidate list fell outside [k, 4096] (heavy ties, score layouts that fool the
+every-16th-pool sample)."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_index_amd import binding as B
+from long_context_sparse_index_amd import inputs as I
+
+from gpu_util import host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ints(shape, lo, hi, rng, dtype):
+    x = torch.from_numpy(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _two_calls(q_i, k_i, w, q_start, p, k):
+    nq = q_i.shape[0]
+    ld = ((max(p, 1) + 3) // 4) * 4
+    scores = torch.empty((nq, ld), dtype=torch.float32, device=q_i.device)
+    B.index_scores(q_i, k_i, w, scores, q_start=q_start, n_pools=p)
+    idx = torch.empty((nq, k), dtype=torch.int32, device=q_i.device)
+    B.topk(scores, idx, q_start=q_start, n_pools=p)
+    return idx
+
+
+def _fused(q_i, k_i, w, q_start, p, k):
+    idx = torch.full((q_i.shape[0], k), -7, dtype=torch.int32, device=q_i.device)
+    B.index_topk(q_i, k_i, w, idx, q_start=q_start, n_pools=p)
+    return idx
+
+
+def _oracle_rows(q_i, k_i, w, q_start, p, k, rows):
+    """Oracle top-k of the given local rows (scores recomputed on the CPU)."""
+    qb = host_bits(q_i.cpu())[rows]
+    kb = host_bits(k_i.cpu())
+    wh = w.cpu().numpy()
+    if wh.ndim == 2:
+        wh = wh[rows]
+    t = q_start + np.asarray(rows, dtype=np.int64)
+    sc = oracle.index_scores(qb, kb, wh, t, p)
+    return oracle.topk(sc, t, p, k)
+
+
+CASES = [
+    # name, p, h_i, d_i, dtype, k, q_start, nq
+    ("tiny_all_visible", 1024, 4, 64, "bf16", 256, 0, 4096),
+    ("sampled_40k", 40000, 8, 128, "bf16", 2048, 100000, 700),
+    ("sampled_70k_32h", 70000, 32, 128, "bf16", 2048, 4 * 70000 - 300, 600),
+    ("fp8_k2051", 40000, 6, 128, "fp8", 2051, 60000, 333),
+    ("d256_k1000", 20000, 3, 256, "bf16", 1000, 70000, 130),
+    ("d32_k1", 9000, 12, 32, "bf16", 1, 30000, 77),
+    ("k2730", 30000, 5, 64, "bf16", 2730, 4 * 30000 - 50, 100),
+    ("boundary_4096", 8192, 4, 64, "bf16", 2048, 4 * 4096 - 40, 80),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_select_matches_two_calls_and_oracle(gpu, case):
+    name, p, h_i, d_i, dtype, k, q_start, nq = case
+    say("case: fused select %s (P=%d, h_i=%d, d_i=%d, %s, k=%d, q_start=%d, nq=%d)" % case)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    r = 8 if dtype == "fp8" else 4
+    q_i = _ints((nq, h_i, d_i), -r, r, rng, dtype).to(gpu)
+    k_i = _ints((p, d_i), -r, r, rng, dtype).to(gpu)
+    # per-row weights, negative ones included: multiples of 1/8 keep every score exact
+    w = torch.from_numpy((rng.integers(-8, 17, size=(nq, h_i)) / 8.0).astype(np.float32)).to(gpu)
+    ref = _two_calls(q_i, k_i, w, q_start, p, k)
+    got = _fused(q_i, k_i, w, q_start, p, k)
+    torch.cuda.synchronize()
+    g, rf = got.cpu().numpy(), ref.cpu().numpy()
+    bad = np.nonzero(np.any(g != rf, axis=1))[0]
+    assert bad.size == 0, "rows %s differ from the two-call path" % bad[:10]
+    rows = np.unique(np.concatenate([[0, nq // 2, nq - 1], rng.integers(0, nq, size=5)]))
+    assert np.array_equal(g[rows], _oracle_rows(q_i, k_i, w, q_start, p, k, rows))
+
+
+@pytest.mark.parametrize("kind", ["all_ties", "few_values", "sample_high", "sample_low",
+                                  "mixed"])
+def test_fused_select_redo_rows(gpu, kind):
+    """Candidate lists outside [k, 4096] send rows to the exact redo."""
+    say("case: fused select redo, %s" % kind)
+    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    p, k, d_i = 20000, 2048, 64
+    q_start, nq = 4 * p - 150, 150  # every row sees all 20000 pools
+    if kind == "all_ties":
+        q_i = torch.zeros((nq, 1, d_i), dtype=torch.bfloat16)
+        k_i = _ints((p, d_i), -4, 4, rng, "bf16")
+    elif kind == "mixed":
+        # rows 40..69 and 130..149 tie everywhere (redone), the others select normally:
+        # only the query tiles holding redone rows are recomputed
+        q_i = _ints((nq, 1, d_i), -4, 4, rng, "bf16")
+        q_i[40:70] = 0
+        q_i[130:150] = 0
+        k_i = _ints((p, d_i), -4, 4, rng, "bf16")
+    elif kind == "few_values":
+        q_i = _ints((nq, 1, d_i), 0, 1, rng, "bf16")
+        k_i = _ints((p, d_i), 0, 1, rng, "bf16")
+    else:
+        # q = 1: the score is the key row's sum; pools that are multiples of 16 (the
+        # threshold sample) get much larger (sample_high: too few candidates) or smaller
+        # (sample_low: far too many) sums than the rest
+        q_i = torch.ones((nq, 1, d_i), dtype=torch.bfloat16)
+        kh = rng.integers(0, 3, size=(p, d_i)).astype(np.float32)
+        kh[::16] += 3.0 if kind == "sample_high" else -3.0
+        k_i = torch.from_numpy(kh).to(torch.bfloat16)
+    q_i, k_i = q_i.to(gpu), k_i.to(gpu)
+    w = torch.ones(1, dtype=torch.float32, device=gpu)
+    ref = _two_calls(q_i, k_i, w, q_start, p, k)
+    got = _fused(q_i, k_i, w, q_start, p, k)
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert np.array_equal(g, ref.cpu().numpy())
+    if kind == "all_ties":  # closed form: the k lowest pools, in order
+        assert np.array_equal(g, np.tile(np.arange(k, dtype=np.int32), (nq, 1)))
+    rows = np.array([0, 45, 100, nq - 1])
+    assert np.array_equal(g[rows], _oracle_rows(q_i, k_i, w, q_start, p, k, rows))
+
+
+def test_fused_select_chunks_and_reuse(gpu):
+    """One workspace reused across chunks of different sizes, as the chunked driver does."""
+    say("case: fused select over chunks with one workspace")
+    rng = np.random.default_rng(11)
+    p, h_i, d_i, k = 12000, 4, 128, 2048
+    n = 4 * p
+    q_i = _ints((n, h_i, d_i), -4, 4, rng, "bf16").to(gpu)
+    k_i = _ints((p, d_i), -4, 4, rng, "bf16").to(gpu)
+    w = I.head_weights(h_i, 4, gpu)
+    chunk = 9000
+    ws = torch.empty(B.index_topk_workspace_bytes(chunk, p, k), dtype=torch.uint8, device=gpu)
+    got = torch.empty((n, k), dtype=torch.int32, device=gpu)
+    for t0 in range(0, n, chunk):
+        nq = min(chunk, n - t0)
+        B.index_topk(q_i[t0:t0 + nq], k_i, w, got[t0:t0 + nq], q_start=t0, n_pools=p, ws=ws)
+    ref = _two_calls(q_i, k_i, w, 0, p, k)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+def test_fused_select_rejects(gpu):
+    say("case: fused select argument errors")
+    q_i = torch.zeros((8, 2, 64), dtype=torch.bfloat16, device=gpu)
+    k_i = torch.zeros((100, 64), dtype=torch.bfloat16, device=gpu)
+    w = torch.ones(2, dtype=torch.float32, device=gpu)
+    idx = torch.empty((8, 2731), dtype=torch.int32, device=gpu)
+    with pytest.raises(B.DSAError) as e:
+        B.index_topk(q_i, k_i, w, idx, q_start=0)
+    assert e.value.status == 2  # unsupported: use the two calls
+    idx = torch.empty((8, 16), dtype=torch.int32, device=gpu)
+    small = torch.empty(256, dtype=torch.uint8, device=gpu)
+    with pytest.raises(B.DSAError) as e:
+        B.index_topk(q_i, k_i, w, idx, q_start=0, ws=small)
+    assert e.value.status == 3
