@@ -318,10 +318,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t p = pw0 + mb * 16 + g * 4 + i;
-          m |= (p < vis && sc[mb][nb][i] >= thr) ? (1u << (mb * 4 + i)) : 0u;
-        }
+        for (int i = 0; i < 4; ++i)
+          m |= sc[mb][nb][i] >= thr ? (1u << (mb * 4 + i)) : 0u;
+      if (pw0 + kPoolsPerWave > vis) {  // tile on the causal boundary: drop invisible pools
+        const int64_t lim = vis - (pw0 + g * 4);  // this lane's pools are pw0 + g*4 + 16 mb + i
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mb * 16 + i >= lim) m &= ~(1u << (mb * 4 + i));
+      }
       mask[nb] = m;
       off[nb] = m ? atomicAdd(&c_cnt[nb * 16 + r16], static_cast<uint32_t>(__builtin_popcount(m)))
                   : 0u;
@@ -339,7 +345,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       uint32_t slot = c_base[nb * 16 + r16] + off[nb];
       uint64_t* const dst = opt.cand + row * opt.cand_cap;
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
+      for (int mb = 0; mb < kMB; ++mb) {
+        if (!((mask[nb] >> (mb * 4)) & 0xFu)) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (mask[nb] & (1u << (mb * 4 + i))) {
@@ -349,6 +356,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
             ++slot;
           }
         }
+      }
     }
     return;
   }

@@ -650,9 +650,10 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
 }
 
 // Per-row threshold for the fused select, from the scores of every 2^shift-th visible pool
-// (sample row of vs = ceil(V / 2^shift) entries): the lower edge of the 22-bit key bin that
-// holds the sample key ranked 1.5 k * vs / V, so that about 1.5 k keys of the full row reach
-// it.  Rows with at most kCand visible pools get threshold 0 (every visible key).  Also
+// (sample row of vs = ceil(V / 2^shift) entries): the lower edge of a key bin (20 bits
+// below the sample's common key prefix, or the top 22 key bits on very long rows) that
+// holds the sample key ranked 1.5 k * vs / V, so that about 1.5 k keys of the full row
+// reach it.  Rows with at most kCand visible pools get threshold 0 (every visible key).  Also
 // zeroes the row's candidate count, and block 0 the any-fallback flag.
 __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(
     const float* __restrict__ sample, int64_t ld_sample, int64_t q_start, int64_t n_pools,
@@ -679,13 +680,103 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(
   uint32_t rank = static_cast<uint32_t>((target * vs + vis / 2) / vis);
   rank = rank < 1u ? 1u : (rank > static_cast<uint32_t>(vs) ? static_cast<uint32_t>(vs) : rank);
   for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-  __syncthreads();
-  auto each_key = [&](auto&& f) {
-    for (int i4 = tid; i4 < vs4; i4 += kTopkThreads) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(srow + 4 * i4);
+  if (vs4 <= 4 * kTopkThreads) {
+    // The whole sample row in registers (four float4 per thread, loaded at once).  Its
+    // smallest and largest keys share their bits above bit hb; the two 10-bit digit windows
+    // start right below that common prefix, so the keys spread over the histogram instead of
+    // piling into the few bins of their shared exponent.
+    uint32_t key[16];
+    uint32_t kmax = 0u, kmin = ~0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i4 = u * kTopkThreads + tid;
+      const f32x4 v = i4 < vs4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = 4 * i4 + e < vs;
+        const uint32_t kk = float_order_key(v[e]);
+        key[4 * u + e] = kk;
+        kmax = ok && kk > kmax ? kk : kmax;
+        kmin = ok && kk < kmin ? kk : kmin;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t omax = __shfl_xor(kmax, off, 64), omin = __shfl_xor(kmin, off, 64);
+      kmax = omax > kmax ? omax : kmax;
+      kmin = omin < kmin ? omin : kmin;
+    }
+    if (tid == 0) {
+      pick[0] = 0u;
+      pick[1] = ~0u;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+      atomicMax(&pick[0], kmax);
+      atomicMin(&pick[1], kmin);
+    }
+    __syncthreads();
+    kmax = pick[0];
+    kmin = pick[1];
+    __syncthreads();  // pick is reused by pick_bin
+    const uint32_t diff = kmax ^ kmin;
+    if (diff == 0u) {  // every sample key equal
+      if (tid == 0) t_est[r] = kmax;
+      return;
+    }
+    const int hb = 31 - __builtin_clz(diff);
+    const uint32_t common = kmax & ~((2u << hb) - 1u);  // bits above hb (2u << 31 == 0)
+    const int sh1 = hb >= 9 ? hb - 9 : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * i4 + e < vs) f(float_order_key(v[e]));
+        if (4 * (u * kTopkThreads + tid) + e < vs)
+          atomicAdd(&hist[(key[4 * u + e] >> sh1) & 0x3FFu], 1u);
+    __syncthreads();
+    uint32_t above1, in1;
+    const uint32_t bin1 = pick_bin(hist, 1024, rank, wave_tmp, pick, &above1, &in1);
+    const uint32_t mask1 = ~((1u << sh1) - 1u);
+    const uint32_t prefix1 = (common | (bin1 << sh1)) & mask1;
+    if (sh1 == 0) {
+      if (tid == 0) t_est[r] = prefix1;
+      return;
+    }
+    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
+    __syncthreads();
+    const int sh2 = sh1 >= 10 ? sh1 - 10 : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * (u * kTopkThreads + tid) + e < vs && (key[4 * u + e] & mask1) == prefix1)
+          atomicAdd(&hist[(key[4 * u + e] >> sh2) & 0x3FFu], 1u);
+    __syncthreads();
+    uint32_t above2, in2;
+    const uint32_t bin2 = pick_bin(hist, 1024, rank - above1, wave_tmp, pick, &above2, &in2);
+    if (tid == 0) t_est[r] = (prefix1 | (bin2 << sh2)) & ~((1u << sh2) - 1u);
+    return;
+  }
+  __syncthreads();
+  // Longer sample rows: two streamed passes over fixed windows (the top 10 key bits, then
+  // the next 10).
+  auto each_key = [&](auto&& f) {
+    for (int base = 0; base < vs4; base += 4 * kTopkThreads) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i4 = base + u * kTopkThreads + tid;
+        v[u] = i4 < vs4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i4 = base + u * kTopkThreads + tid;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * i4 + e < vs) f(float_order_key(v[u][e]));
+      }
     }
   };
   each_key([&](uint32_t key) { atomicAdd(&hist[key >> 22], 1u); });
