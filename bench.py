@@ -25,6 +25,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# The chunked forward selects through the fused indexer -> top-k path (dsa_index_topk) for
+# chunks whose first row sees at least this many pools, when k allows it; the same rule is
+# applied here to time the select the way the driver runs it.
+FUSED_MIN_VISIBLE = 49152
+FUSED_MAX_K = 2730
+
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
@@ -138,9 +144,31 @@ def main():
                          device=dev)
     scores = torch.empty((chunk, ld), dtype=torch.float32, device=dev)
     idx_chunk = torch.empty((chunk, k), dtype=torch.int32, device=dev)
+    sel_ws = (torch.empty(B.index_topk_workspace_bytes(chunk, p, k), dtype=torch.uint8,
+                          device=dev) if k <= FUSED_MAX_K else None)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     chunks = chunk_ranges(n, chunk)
+
+    def uses_fused(t0):
+        return sel_ws is not None and min(p, (t0 + 1) // 4) >= FUSED_MIN_VISIBLE
+
+    def step_select(rec):
+        """The select of every chunk as the chunked driver runs it (events per chunk when
+        rec is a list)."""
+        for t0, nq in chunks:
+            if rec is not None:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+            if uses_fused(t0):
+                B.index_topk(q_i[t0:t0 + nq], k_i, w, idx_chunk[:nq], q_start=t0, n_pools=p,
+                             ws=sel_ws)
+            else:
+                B.index_scores(q_i[t0:t0 + nq], k_i, w, scores[:nq], q_start=t0)
+                B.topk(scores[:nq], idx_chunk[:nq], q_start=t0, n_pools=p)
+            if rec is not None:
+                e[1].record(stream)
+                rec.append((uses_fused(t0), e))
 
     def step_driver():
         B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=k, chunk=chunk, scale=wl.scale,
@@ -160,7 +188,7 @@ def main():
             e[3].record(stream)
             events.append((t0, nq, e))
 
-    step = step_driver if has_attn else (lambda: step_phases([]))
+    step = step_driver if has_attn else (lambda: step_select(None))
 
     # ---- timed region: whole forward steps
     for _ in range(args.warmup):
@@ -191,6 +219,13 @@ def main():
         ph_ms["attn_fwd"] += e[2].elapsed_time(e[3])
     per_step = {kname: v / args.steps for kname, v in ph_ms.items()}
     n_launch = len(chunks)
+    # ---- the select (indexer + top-k) per chunk as the driver runs it
+    sel_rec = []
+    for _ in range(args.steps):
+        step_select(sel_rec)
+    torch.cuda.synchronize()
+    sel_fused = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if f) / args.steps
+    sel_two = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if not f) / args.steps
 
     # algorithmic work of one step
     pairs = visible_pairs(0, n, p)
@@ -222,6 +257,14 @@ def main():
                  "frac_of_hbm_peak": gbs(topk_bytes, per_step["topk"]) / PEAK_HBM_GBS,
                  "tokens_per_s": n / (per_step["topk"] * 1e-3)},
     }
+    n_fused = sum(1 for t0, _ in chunks if uses_fused(t0))
+    phases["select"] = {
+        "ms_per_step": sel_fused + sel_two, "fused_chunks": n_fused, "chunks": n_launch,
+        "fused_ms_per_step": sel_fused, "score_row_ms_per_step": sel_two,
+        "tokens_per_s": n / ((sel_fused + sel_two) * 1e-3),
+        "note": "indexer + top-k of every chunk as dsa_forward_chunked runs them: the fused "
+                "select (dsa_index_topk) on chunks whose rows see >= %d pools, else "
+                "dsa_index_scores + dsa_topk (the two phases above)" % FUSED_MIN_VISIBLE}
     if has_attn:
         phases["attn_fwd"] = {
             "ms_per_step": per_step["attn_fwd"], "avg_launch_ms": per_step["attn_fwd"] / n_launch,
@@ -260,7 +303,8 @@ def main():
 
     value = n / (ms_per_step * 1e-3)
     line = {
-        "metric": "DSA forward tokens/s (indexer + top-k + sparse attention, chunked)",
+        "metric": ("DSA forward tokens/s (indexer + top-k + sparse attention, chunked)"
+                   if has_attn else "DSA select tokens/s (indexer + top-k, chunked)"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
