@@ -163,3 +163,42 @@ def test_fused_select_rejects(gpu):
     with pytest.raises(B.DSAError) as e:
         B.index_topk(q_i, k_i, w, idx, q_start=0, ws=small)
     assert e.value.status == 3
+
+
+def test_chunked_forward_mixes_fused_and_two_call_chunks(gpu):
+    """dsa_forward_chunked takes the fused select only on chunks whose first row sees at
+    least 49152 pools: with P = 52000 and chunks of 50000 queries only the last chunk does.
+    Indices of every row must equal the two-call path, and the attention output is then the
+    same kernel on the same indices (bit-identical)."""
+    from long_context_sparse_index_amd import workloads as W
+
+    say("case: chunked forward, P=52000, chunk 50000 (last chunk fused)")
+    base = W.WORKLOADS["tiny_4k"]
+    p = 52000
+    wl = W.Workload(name="mixed", n_tokens=4 * p, n_pools=p, h_i=4, d_i=64,
+                    index_dtype="bf16", int_range=4, w_period=4, topk=2048, heads=8,
+                    d_qk=128, d_v=128, scale=base.scale, chunk=50000)
+    q_i, k_i, w = I.index_inputs(wl, gpu)
+    q, kv, _ = I.attn_inputs(wl, gpu)
+    n, k = wl.n_tokens, wl.topk
+    o = torch.empty((n, wl.heads, wl.d_v), dtype=torch.float32, device=gpu)
+    lse = torch.empty((n, wl.heads), dtype=torch.float32, device=gpu)
+    idx = torch.empty((n, k), dtype=torch.int32, device=gpu)
+    B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=k, chunk=wl.chunk, scale=wl.scale,
+                      d_v=wl.d_v, idx_out=idx)
+    ref_idx = torch.empty_like(idx)
+    for t0 in range(0, n, wl.chunk):
+        nq = min(wl.chunk, n - t0)
+        ref_idx[t0:t0 + nq] = _two_calls(q_i[t0:t0 + nq], k_i, w, t0, p, k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref_idx)
+    o_ref = torch.empty_like(o)
+    lse_ref = torch.empty_like(lse)
+    B.sparse_attn_fwd(q, kv, ref_idx, o_ref, lse_ref, scale=wl.scale, d_v=wl.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int32), o_ref.view(torch.int32))
+    rows = np.array([4 * p - 1, 200001, 150000, 49999])
+    qb = host_bits(q_i[torch.from_numpy(rows).to(gpu)].cpu())
+    sc = oracle.index_scores(qb, host_bits(k_i.cpu()), w.cpu().numpy(), rows, p)
+    assert np.array_equal(idx[torch.from_numpy(rows).to(gpu)].cpu().numpy(),
+                          oracle.topk(sc, rows, p, k))
