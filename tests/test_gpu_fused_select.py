@@ -202,3 +202,37 @@ def test_chunked_forward_mixes_fused_and_two_call_chunks(gpu):
     sc = oracle.index_scores(qb, host_bits(k_i.cpu()), w.cpu().numpy(), rows, p)
     assert np.array_equal(idx[torch.from_numpy(rows).to(gpu)].cpu().numpy(),
                           oracle.topk(sc, rows, p, k))
+
+
+def test_chunked_forward_large_k_takes_two_call_select(gpu):
+    """k above 2730 has no fused select: dsa_forward_chunked selects with dsa_index_scores +
+    dsa_topk inside the same workspace layout; its indices and outputs must equal the
+    separate calls."""
+    from long_context_sparse_index_amd import workloads as W
+
+    say("case: chunked forward, k=3000 (two-call select), P=6000, chunk 7000")
+    base = W.WORKLOADS["tiny_4k"]
+    p = 6000
+    wl = W.Workload(name="large_k", n_tokens=4 * p, n_pools=p, h_i=4, d_i=64,
+                    index_dtype="bf16", int_range=4, w_period=4, topk=3000, heads=8,
+                    d_qk=128, d_v=128, scale=base.scale, chunk=7000)
+    q_i, k_i, w = I.index_inputs(wl, gpu)
+    q, kv, _ = I.attn_inputs(wl, gpu)
+    n, k = wl.n_tokens, wl.topk
+    o = torch.empty((n, wl.heads, wl.d_v), dtype=torch.float32, device=gpu)
+    lse = torch.empty((n, wl.heads), dtype=torch.float32, device=gpu)
+    idx = torch.empty((n, k), dtype=torch.int32, device=gpu)
+    B.forward_chunked(q_i, k_i, w, q, kv, o, lse, k=k, chunk=wl.chunk, scale=wl.scale,
+                      d_v=wl.d_v, idx_out=idx)
+    ref_idx = _two_calls(q_i, k_i, w, 0, p, k)
+    o_ref = torch.empty_like(o)
+    lse_ref = torch.empty_like(lse)
+    B.sparse_attn_fwd(q, kv, ref_idx, o_ref, lse_ref, scale=wl.scale, d_v=wl.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref_idx)
+    assert torch.equal(o.view(torch.int32), o_ref.view(torch.int32))
+    rows = np.array([3, 4 * 3000 + 1, n - 1])
+    qb = host_bits(q_i[torch.from_numpy(rows).to(gpu)].cpu())
+    sc = oracle.index_scores(qb, host_bits(k_i.cpu()), w.cpu().numpy(), rows, p)
+    assert np.array_equal(idx[torch.from_numpy(rows).to(gpu)].cpu().numpy(),
+                          oracle.topk(sc, rows, p, k))
