@@ -293,8 +293,10 @@ def main():
                 "traffic": recorded_traffic("attn_fwd", wl.name)}
 
     if has_attn and "attn_bwd" in wl.phases:
-        phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_for_bwd(wl, q_i, k_i, w, dev),
-                                           args.steps, stream)
+        idx_b = idx_for_bwd(wl, q_i, k_i, w, dev)
+        phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_b, args.steps, stream)
+        phases["attn_bwd_deterministic"] = time_backward(wl, q, kv, o, lse, idx_b, args.steps,
+                                                         stream, deterministic=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -346,9 +348,10 @@ def idx_for_bwd(wl, q_i, k_i, w, dev):
     return idx
 
 
-def time_backward(wl, q, kv, o, lse, idx, steps, stream):
-    """Times dsa_sparse_attn_bwd over the whole sequence (dQ, and dK / dV by fp32 atomics)
-    on the forward's outputs; flops count the recomputed logits, dP, dV, dQ and dK."""
+def time_backward(wl, q, kv, o, lse, idx, steps, stream, deterministic=False):
+    """Times dsa_sparse_attn_bwd over the whole sequence (dQ, and dK / dV by fp32 atomics;
+    or dsa_sparse_attn_bwd_deterministic, fixed-point dK / dV) on the forward's outputs;
+    flops count the recomputed logits, dP, dV, dQ and dK."""
     import torch
 
     from long_context_sparse_index_amd import binding as B
@@ -359,14 +362,18 @@ def time_backward(wl, q, kv, o, lse, idx, steps, stream):
     d_o = I.grad_output(wl, q.device)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dkv = torch.zeros((p, wl.d_qk), dtype=torch.float32, device=q.device)
-    ws = torch.empty(B.sparse_attn_bwd_workspace_bytes(n, wl.heads), dtype=torch.uint8,
-                     device=q.device)
+    if deterministic:
+        ws = torch.empty(B.sparse_attn_bwd_deterministic_workspace_bytes(
+            n, wl.heads, p, wl.d_qk, wl.d_v, False), dtype=torch.uint8, device=q.device)
+    else:
+        ws = torch.empty(B.sparse_attn_bwd_workspace_bytes(n, wl.heads), dtype=torch.uint8,
+                         device=q.device)
+    bwd = B.sparse_attn_bwd_deterministic if deterministic else B.sparse_attn_bwd
 
     def run():
         # V is the first d_v columns of the latent row: its gradient folds into dKV
         dkv.zero_()
-        B.sparse_attn_bwd(q, kv, idx, o, lse, d_o, dq, dkv, scale=wl.scale, d_v=wl.d_v,
-                          ws=ws)
+        bwd(q, kv, idx, o, lse, d_o, dq, dkv, scale=wl.scale, d_v=wl.d_v, ws=ws)
 
     run()
     torch.cuda.synchronize()
@@ -383,8 +390,9 @@ def time_backward(wl, q, kv, o, lse, idx, steps, stream):
     return {"ms_per_step": ms, "tflops": flop / (ms * 1e-3) / 1e12,
             "frac_of_mfma_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "tokens_per_s": n / (ms * 1e-3),
-            "note": "dsa_sparse_attn_bwd over all rows (dQ, dKV with dV folded in), timed "
-                    "with the zeroing of dKV, %d launches" % steps}
+            "note": "%s over all rows (dQ, dKV with dV folded in), timed with the zeroing of "
+                    "dKV, %d launches" % ("dsa_sparse_attn_bwd_deterministic" if deterministic
+                                          else "dsa_sparse_attn_bwd", steps)}
 
 
 def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):

@@ -197,6 +197,31 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, con
 size_t dsa_sparse_attn_bwd_workspace_bytes(int64_t nq, int32_t h);
 
 /*
+ * dsa_sparse_attn_bwd_deterministic - dsa_sparse_attn_bwd with results that do not vary from
+ * run to run (bit-identical dq, dkv, dv for the same inputs).  The pages train the layer but
+ * print no backward; reproducible gradients are this library's option.  dK and dV are
+ * accumulated as signed 64-bit fixed-point numbers with 32 fractional bits (each
+ * contribution rounded to a multiple of 2^-32, added with integer atomics, whose sum does
+ * not depend on the order), then added into dkv (and dv) in fp32, one rounding per element.
+ *   Arguments as dsa_sparse_attn_bwd (dkv and dv are still accumulated: the caller zeroes
+ *   them or keeps a running sum).
+ *   ws: at least dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk, d_v,
+ *   separate_v = (dv != NULL)) bytes, 256-byte aligned: the per-row deltas plus 8 bytes per
+ *   dkv (and dv) element.
+ *   Range: every partial sum of one element must stay below 2^31 in magnitude (a larger one
+ *   wraps around); contributions below 2^-33 in magnitude are dropped.
+ *   Supported: as the forward.
+ */
+dsa_status dsa_sparse_attn_bwd_deterministic(
+    const void* q, const void* kv, int64_t ld_kv, const void* v, int64_t ld_v,
+    const int32_t* idx, int32_t k, const void* o, int32_t o_dtype, const float* lse,
+    const void* d_o, float* dq, float* dkv, float* dv, int64_t nq, int64_t n_pools, int32_t h,
+    int32_t d_qk, int32_t d_v, float scale, void* ws, size_t ws_bytes, void* stream);
+size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
+                                                         int64_t n_pools, int32_t d_qk,
+                                                         int32_t d_v, int32_t separate_v);
+
+/*
  * dsa_forward_chunked - the whole DSA forward over n_tokens queries, one query chunk at a
  * time: for each chunk [t0, t0 + chunk) it runs the select (dsa_index_topk when k <= 2730,
  * else dsa_index_scores into one reused fp32 score buffer in the workspace and dsa_topk),

@@ -54,6 +54,11 @@ _SIGNATURES = {
     "dsa_sparse_attn_bwd": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
                              _I64, _I64, _I32, _I32, _I32, _F32, _P, _SZ, _P], ctypes.c_int),
     "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32], _SZ),
+    "dsa_sparse_attn_bwd_deterministic": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P,
+                                           _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _F32, _P,
+                                           _SZ, _P], ctypes.c_int),
+    "dsa_sparse_attn_bwd_deterministic_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32, _I32],
+                                                          _SZ),
     "dsa_forward_chunked": ([_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P,
                              _I64, _I32, _I32, _I32, _F32, _I32, _I64, _I64, _I64, _P, _I32, _P,
                              _P, _P, _SZ, _P], ctypes.c_int),
@@ -225,6 +230,34 @@ def sparse_attn_bwd(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
                                    nq, n_pools, h, d_qk, d_v, float(scale), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(stream)))
+    return dq, dkv, dv
+
+
+def sparse_attn_bwd_deterministic_workspace_bytes(nq: int, h: int, n_pools: int, d_qk: int,
+                                                  d_v: int, separate_v: bool) -> int:
+    return int(load_library().dsa_sparse_attn_bwd_deterministic_workspace_bytes(
+        nq, h, n_pools, d_qk, d_v, int(separate_v)))
+
+
+def sparse_attn_bwd_deterministic(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
+                                  v=None, dv=None, n_pools: int | None = None, ws=None,
+                                  stream=None):
+    """As sparse_attn_bwd, with run-to-run identical dq, dkv and dv (fixed-point dK/dV
+    accumulation)."""
+    nq, h, d_qk = q.shape
+    n_pools = kv.shape[0] if n_pools is None else n_pools
+    for t in (q, idx, o, lse, d_o, dq, dkv):
+        assert t.is_contiguous()
+    if ws is None:
+        need = sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk, d_v,
+                                                             dv is not None)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check(lib.dsa_sparse_attn_bwd_deterministic(
+        _ptr(q), _ptr(kv), kv.stride(0), _ptr(v), 0 if v is None else v.stride(0), _ptr(idx),
+        idx.shape[1], _ptr(o), _out_code(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dkv),
+        _ptr(dv), nq, n_pools, h, d_qk, d_v, float(scale), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return dq, dkv, dv
 
 

@@ -321,6 +321,45 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, con
                     "dsa_sparse_attn_bwd launch");
 }
 
+size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
+                                                         int64_t n_pools, int32_t d_qk,
+                                                         int32_t d_v, int32_t separate_v) {
+  if (d_qk <= 0 || d_v <= 0) return 0;
+  return align256(dsa::attn_bwd_workspace_bytes(nq, h)) +
+         dsa::attn_bwd_fixed_bytes(n_pools, d_qk, d_v, separate_v != 0);
+}
+
+dsa_status dsa_sparse_attn_bwd_deterministic(
+    const void* q, const void* kv, int64_t ld_kv, const void* v, int64_t ld_v,
+    const int32_t* idx, int32_t k, const void* o, int32_t o_dtype, const float* lse,
+    const void* d_o, float* dq, float* dkv, float* dv, int64_t nq, int64_t n_pools, int32_t h,
+    int32_t d_qk, int32_t d_v, float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (dsa_status st = check_attn_args(q, kv, ld_kv, v, ld_v, idx, k, n_pools, h, d_qk, d_v,
+                                      scale))
+    return st;
+  if (dsa_status st = check_out_dtype(o_dtype)) return st;
+  DSA_REQUIRE(o && lse && d_o && dq && dkv, "attn_bwd_det: null o, lse, d_o, dq or dkv");
+  DSA_REQUIRE(aligned(o, 16) && aligned(d_o, 16) && aligned(dq, 16) && aligned(dkv, 16) &&
+                  aligned(lse, 4),
+              "attn_bwd_det: o, d_o, dq, dkv must be 16-byte aligned");
+  DSA_REQUIRE(!v || dv, "attn_bwd_det: dv is required when a separate v is given");
+  DSA_REQUIRE(!dv || aligned(dv, 16), "attn_bwd_det: dv must be 16-byte aligned");
+  DSA_REQUIRE(nq >= 0, "attn_bwd_det: nq must be >= 0");
+  const size_t need = dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk,
+                                                                        d_v, dv != nullptr);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(DSA_ERR_WORKSPACE,
+                "attn_bwd_det: 256-byte aligned workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : size_t{0});
+  char* base = static_cast<char*>(ws);
+  void* fixed = base + align256(dsa::attn_bwd_workspace_bytes(nq, h));
+  return hip_status(dsa::launch_sparse_attn_bwd(q, kv, ld_kv, v, ld_v, idx, k, o,
+                                                o_dtype == DSA_DTYPE_F32, lse, d_o, dq, dkv,
+                                                dv, nq, n_pools, h, d_qk, d_v, scale, ws,
+                                                static_cast<hipStream_t>(stream), fixed),
+                    "dsa_sparse_attn_bwd_deterministic launch");
+}
+
 size_t dsa_index_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k) {
   if (nq <= 0 || k <= 0 || n_pools < 0) return 0;
   return fused_layout(nq, n_pools).total;

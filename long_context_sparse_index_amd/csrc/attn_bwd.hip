@@ -226,12 +226,29 @@ __device__ __forceinline__ bf16x8 heads_operand(const uint16_t* x, int ld, int k
   return join_tr(lo, hi);
 }
 
-template <int DQK, int DV, bool SEPARATE_V>
+// Deterministic accumulation: each contribution becomes a signed 64-bit fixed-point value
+// with 32 fractional bits (value * 2^32, rounded to nearest), added with integer atomics.
+// Integer addition is associative, so the sums do not depend on the order in which tokens
+// arrive; a second pass converts them to fp32 once.  Valid while every partial sum stays
+// below 2^31 in magnitude; values below 2^-33 are lost.
+constexpr float kFixedScale = 4294967296.0f;  // 2^32
+
+template <bool FIXED>
+__device__ __forceinline__ void grad_add(void* base, int64_t i, float val) {
+  if constexpr (FIXED) {
+    const long long fx = __float2ll_rn(val * kFixedScale);
+    atomicAdd(static_cast<unsigned long long*>(base) + i, static_cast<unsigned long long>(fx));
+  } else {
+    atomicAdd(static_cast<float*>(base) + i, val);
+  }
+}
+
+template <int DQK, int DV, bool SEPARATE_V, bool FIXED>
 __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
-    const float* __restrict__ delta, float* __restrict__ dkv, float* __restrict__ dv,
+    const float* __restrict__ delta, void* __restrict__ dkv, void* __restrict__ dv,
     int64_t n_pools, int h, float scale_log2, float scale) {
   using Lds = DkvLds<DQK, DV, SEPARATE_V>;
   using Dma = typename Lds::Dma;
@@ -368,12 +385,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (dst[i] < 0) continue;
-          float* krow = dkv + static_cast<int64_t>(dst[i]) * DQK;
+          const int64_t kat = static_cast<int64_t>(dst[i]) * DQK + col;
           if (fold_v) {
-            atomicAdd(krow + col, ak[i] * scale + (col0 < DV ? av[i] : 0.0f));
+            grad_add<FIXED>(dkv, kat, ak[i] * scale + (col0 < DV ? av[i] : 0.0f));
           } else {
-            atomicAdd(krow + col, ak[i] * scale);
-            if (col0 < DV) atomicAdd(dv + static_cast<int64_t>(dst[i]) * DV + col, av[i]);
+            grad_add<FIXED>(dkv, kat, ak[i] * scale);
+            if (col0 < DV) grad_add<FIXED>(dv, static_cast<int64_t>(dst[i]) * DV + col, av[i]);
           }
         }
       }
@@ -381,12 +398,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   });
 }
 
+// Fixed-point accumulators: cleared by a fill kernel (a memset node is avoided so that the
+// launch sequence can be captured in a graph), then added into the caller's fp32 buffer.
+__global__ __launch_bounds__(256) void fixed_zero_kernel(unsigned long long* __restrict__ a,
+                                                         int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    a[i] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void fixed_to_f32_add_kernel(
+    const unsigned long long* __restrict__ a, float* __restrict__ out, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const double v = static_cast<double>(static_cast<long long>(a[i])) * (1.0 / 4294967296.0);
+    out[i] += static_cast<float>(v);
+  }
+}
+
+unsigned fill_grid(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return static_cast<unsigned>(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
 template <int DQK, int DV, bool SEP>
 hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void* v,
                         int64_t ld_v, const int32_t* idx, int k, const void* o, int o_f32,
                         const float* lse, const void* d_o, float* dq, float* dkv, float* dv,
                         int64_t nq, int64_t n_pools, int h, float scale, float* delta,
-                        hipStream_t stream) {
+                        unsigned long long* fixed, hipStream_t stream) {
   const int64_t rows = nq * h;
   const unsigned dgrid = static_cast<unsigned>((rows + 3) / 4);
   if (o_f32)
@@ -405,11 +445,37 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
                      sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP>), dim3(static_cast<unsigned>(nq)),
+  if (!fixed) {
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, false>),
+                       dim3(static_cast<unsigned>(nq)), dim3(kAttnThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), ld_kv,
+                       static_cast<const uint16_t*>(v), ld_v, idx, k, lse,
+                       static_cast<const uint16_t*>(d_o), delta, static_cast<void*>(dkv),
+                       static_cast<void*>(dv), n_pools, h, sl2, scale);
+    return hipGetLastError();
+  }
+  // Deterministic: fixed-point accumulators [n_pools, DQK] (and [n_pools, DV] for a
+  // separate dv) in the workspace.
+  const int64_t nk = n_pools * DQK, nv = dv ? n_pools * DV : 0;
+  unsigned long long* fk = fixed;
+  unsigned long long* fv = dv ? fixed + nk : nullptr;
+  hipLaunchKernelGGL(fixed_zero_kernel, dim3(fill_grid(nk + nv)), dim3(256), 0, stream, fixed,
+                     nk + nv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, true>), dim3(static_cast<unsigned>(nq)),
                      dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
-                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta, dkv, dv,
-                     n_pools, h, sl2, scale);
+                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta,
+                     static_cast<void*>(fk), static_cast<void*>(fv), n_pools, h, sl2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fixed_to_f32_add_kernel, dim3(fill_grid(nk)), dim3(256), 0, stream, fk,
+                     dkv, nk);
+  e = hipGetLastError();
+  if (e != hipSuccess || !dv) return e;
+  hipLaunchKernelGGL(fixed_to_f32_add_kernel, dim3(fill_grid(nv)), dim3(256), 0, stream, fv, dv,
+                     nv);
   return hipGetLastError();
 }
 
@@ -419,21 +485,29 @@ size_t attn_bwd_workspace_bytes(int64_t nq, int h) {
   return static_cast<size_t>(nq > 0 ? nq : 0) * static_cast<size_t>(h > 0 ? h : 0) * sizeof(float);
 }
 
+size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v) {
+  const int64_t p = n_pools > 0 ? n_pools : 0;
+  return static_cast<size_t>(p) * static_cast<size_t>(d_qk + (separate_v ? d_v : 0)) *
+         sizeof(unsigned long long);
+}
+
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
                                   int64_t ld_v, const int32_t* idx, int k, const void* o,
                                   int o_f32, const float* lse, const void* d_o, float* dq,
                                   float* dkv, float* dv, int64_t nq, int64_t n_pools, int h,
                                   int d_qk, int d_v, float scale, void* ws,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, void* fixed_ws) {
   if (nq <= 0) return hipSuccess;
   if (nq * h >= (int64_t{1} << 33)) return hipErrorInvalidConfiguration;
   float* delta = static_cast<float*>(ws);
+  unsigned long long* fixed = static_cast<unsigned long long*>(fixed_ws);
 #define DSA_BWD(DQ, DVV)                                                                      \
   return v ? launch_bwd_t<DQ, DVV, true>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, d_o,   \
-                                         dq, dkv, dv, nq, n_pools, h, scale, delta, stream)   \
+                                         dq, dkv, dv, nq, n_pools, h, scale, delta, fixed,    \
+                                         stream)                                              \
            : launch_bwd_t<DQ, DVV, false>(q, kv, ld_kv, nullptr, 0, idx, k, o, o_f32, lse,    \
                                           d_o, dq, dkv, dv, nq, n_pools, h, scale, delta,     \
-                                          stream)
+                                          fixed, stream)
   if (d_qk == 128 && d_v == 128) DSA_BWD(128, 128);
   if (d_qk == 576 && d_v == 512) DSA_BWD(576, 512);
   if (d_qk == 512 && d_v == 512) DSA_BWD(512, 512);

@@ -67,10 +67,15 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* kv, int64_t ld_kv, 
                                   int d_v, float scale, hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(int64_t nq, int h);
+// Bytes of the fixed-point dK (and separate dV) accumulators of the deterministic backward.
+size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v);
+// fixed_ws (non-null): deterministic dK/dV through 64-bit fixed-point accumulators of
+// attn_bwd_fixed_bytes(...) bytes, 8-byte aligned; null: fp32 atomics.
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
                                   int64_t ld_v, const int32_t* idx, int k, const void* o,
                                   int o_f32, const float* lse, const void* d_o, float* dq, float* dkv,
                                   float* dv, int64_t nq, int64_t n_pools, int h, int d_qk,
-                                  int d_v, float scale, void* ws, hipStream_t stream);
+                                  int d_v, float scale, void* ws, hipStream_t stream,
+                                  void* fixed_ws = nullptr);
 
 }  // namespace dsa
