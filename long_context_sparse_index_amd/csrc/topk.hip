@@ -183,6 +183,24 @@ __device__ __forceinline__ void sort_keys(uint64_t* buf, uint64_t* alt, int n2) 
     bitonic_sort_regs<4>(buf, alt);
 }
 
+// First digit window of a select over keys known to lie in [lo, hi]: they share the bits
+// above the highest bit where lo and hi differ (mask, prefix), and the 10-bit window ends at
+// that bit, so the keys spread over the histogram instead of piling into the few bins of a
+// shared exponent (fewer digit rounds and fewer colliding LDS atomics).
+__device__ __forceinline__ void digit_window(uint32_t lo, uint32_t hi, uint32_t* mask,
+                                             uint32_t* prefix, int* shift) {
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0u) {  // one key value: a single window over the low bits, ties by pool
+    *mask = 0xFFFFFC00u;
+    *shift = 0;
+  } else {
+    const int hb = 31 - __builtin_clz(diff);
+    *mask = ~((2u << hb) - 1u);  // 2u << 31 == 0: no shared bits
+    *shift = hb >= 9 ? hb - 9 : 0;
+  }
+  *prefix = lo & *mask;
+}
+
 __device__ __forceinline__ int next_pow2(int n) {
   int p = 1;
   while (p < n) p <<= 1;
@@ -378,18 +396,9 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     if (my_max) atomicMax(&cand_max, my_max);
     __syncthreads();
     const uint32_t t_est = cs.t_est[r];
-    const uint32_t diff = t_est ^ cand_max;
-    uint32_t prefix = 0u, mask = 0u;
-    int shift = 22;
-    if (diff < (1u << 22)) {
-      mask = 0xFFC00000u;
-      shift = 12;
-      if (diff < (1u << 12)) {
-        mask = 0xFFFFF000u;
-        shift = 2;
-      }
-      prefix = t_est & mask;
-    }
+    uint32_t mask, prefix;
+    int shift;
+    digit_window(t_est, cand_max, &mask, &prefix, &shift);
     resolve_candidates(static_cast<int>(n), prefix, mask, k, shift);
     const int n2 = max(next_pow2(k), kTopkThreads);
     for (int i = k + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
@@ -508,19 +517,10 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     __syncthreads();  // fill[] is reset below
     if (sampled) {
       // The candidates lie in [t_est, cand_max]: the top bits those two share are fixed, and
-      // the select starts at the first 10-bit window where they differ.
-      const uint32_t diff = t_est ^ cand_max;
-      uint32_t prefix = 0u, mask = 0u;
-      int shift = 22;
-      if (diff < (1u << 22)) {
-        mask = 0xFFC00000u;
-        shift = 12;
-        if (diff < (1u << 12)) {
-          mask = 0xFFFFF000u;
-          shift = 2;
-        }
-        prefix = t_est & mask;
-      }
+      // the select starts right below them.
+      uint32_t mask, prefix;
+      int shift;
+      digit_window(t_est, cand_max, &mask, &prefix, &shift);
       resolve_candidates(static_cast<int>(n_cand), prefix, mask, k, shift);
     }
   }
