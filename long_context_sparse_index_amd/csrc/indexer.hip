@@ -180,11 +180,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   }
 
   // Head weights of the tile's queries, stored [head][query] so that the 16 lanes of a group
-  // read 16 consecutive words.
+  // read 16 consecutive words; consecutive threads write consecutive words (walking the
+  // rows of one head first avoids 32-way bank conflicts on the transposing stores).
   for (int i = tid; i < kBQ * h_i; i += kIdxThreads) {
-    const int row = i / h_i;
-    const int j = i - row * h_i;
-    w_lds[j * kBQ + row] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
+    const int j = i / kBQ;
+    const int row = i - j * kBQ;
+    w_lds[i] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
   }
 
   // This wave's pooled key rows, resident for all heads.
