@@ -170,7 +170,7 @@ hipError_t run_fused_select(const void* q_idx, int64_t q_row_stride, const void*
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.cand);
   uint32_t* t_est = reinterpret_cast<uint32_t*>(ws + L.t_est);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
-  int32_t* fail = reinterpret_cast<int32_t*>(ws + L.fail);
+  int32_t* redo = reinterpret_cast<int32_t*>(ws + L.fail);
   int32_t* any = reinterpret_cast<int32_t*>(ws + L.any);
   float* scores = reinterpret_cast<float*>(ws + L.scores);
 
@@ -196,17 +196,17 @@ hipError_t run_fused_select(const void* q_idx, int64_t q_row_stride, const void*
   cs.cap = dsa::topk_cand_cap();
   cs.cnt = cnt;
   cs.t_est = t_est;
-  cs.fail = fail;
+  cs.fail = redo;
   cs.any_fail = any;
   e = dsa::launch_topk_from_cand(cs, q_start, nq, n_pools, k, idx, s);
   if (e != hipSuccess) return e;
   dsa::IndexerOpts gopt;
   gopt.gate = any;
-  gopt.gate_rows = fail;
+  gopt.gate_rows = redo;
   e = dsa::launch_index_scores(q_idx, q_row_stride, k_idx, k_row_stride, w, w_row_stride,
                                scores, L.ld, q_start, nq, n_pools, h_i, d_i, dtype, 0, s, gopt);
   if (e != hipSuccess) return e;
-  return dsa::launch_topk(scores, L.ld, q_start, nq, n_pools, k, idx, nullptr, 0, s, fail);
+  return dsa::launch_topk(scores, L.ld, q_start, nq, n_pools, k, idx, nullptr, 0, s, redo);
 }
 
 dsa_status check_out_dtype(int32_t o_dtype) {
