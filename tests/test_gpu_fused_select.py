@@ -236,3 +236,51 @@ def test_chunked_forward_large_k_takes_two_call_select(gpu):
     sc = oracle.index_scores(qb, host_bits(k_i.cpu()), w.cpu().numpy(), rows, p)
     assert np.array_equal(idx[torch.from_numpy(rows).to(gpu)].cpu().numpy(),
                           oracle.topk(sc, rows, p, k))
+
+
+def test_index_topk_256k_fp8_full_size_sampled(gpu):
+    """The fp8 indexer + top-k workload at full size (N = 262144, P = 65536, 32 x 128 e4m3
+    indexer, k = 2048, chunks of 16384), selected as the chunked driver does: the fused
+    select on chunks whose rows see >= 49152 pools, the two calls elsewhere.  Structure on
+    every row; sampled rows bit-exact against the oracle; the fused chunks also against the
+    two-call path on all their rows."""
+    from long_context_sparse_index_amd import workloads as W
+
+    wl = W.WORKLOADS["index_topk_256k_fp8"]
+    n, p, k, chunk = wl.n_tokens, wl.n_pools, wl.topk, wl.chunk
+    say("case: index_topk_256k_fp8 full size (N=%d, P=%d), chunk %d" % (n, p, chunk))
+    q_i, k_i, w = I.index_inputs(wl, gpu)
+    idx = torch.empty((n, k), dtype=torch.int32, device=gpu)
+    ws = torch.empty(B.index_topk_workspace_bytes(chunk, p, k), dtype=torch.uint8, device=gpu)
+    n_fused = 0
+    for t0 in range(0, n, chunk):
+        nq = min(chunk, n - t0)
+        if min(p, (t0 + 1) // 4) >= 49152:
+            B.index_topk(q_i[t0:t0 + nq], k_i, w, idx[t0:t0 + nq], q_start=t0, n_pools=p, ws=ws)
+            ref = _two_calls(q_i[t0:t0 + nq], k_i, w, t0, p, k)
+            assert torch.equal(idx[t0:t0 + nq], ref), "fused chunk at %d differs" % t0
+            n_fused += 1
+        else:
+            idx[t0:t0 + nq] = _two_calls(q_i[t0:t0 + nq], k_i, w, t0, p, k)
+    torch.cuda.synchronize()
+    say("  select done (%d fused chunks, equal to the two calls)" % n_fused)
+    assert n_fused == 4
+    slot = torch.arange(k, device=gpu)
+    for r0 in range(0, n, 65536):
+        blk = idx[r0:r0 + 65536]
+        t = torch.arange(r0, r0 + blk.shape[0], device=gpu, dtype=torch.int64)
+        vis = torch.clamp((t + 1) // 4, max=p)
+        c = torch.clamp(vis, max=k)
+        valid = blk >= 0
+        assert torch.equal(valid.sum(1), c)
+        assert torch.equal(valid, slot[None, :] < c[:, None])
+        assert bool((blk.long() < vis[:, None]).all())
+        srt = torch.sort(blk, dim=1).values
+        assert not bool(((srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] >= 0)).any())
+    say("  structure ok on all %d rows" % n)
+    rows = I.sample_rows(wl, n_uniform=16)
+    rt = torch.from_numpy(rows).to(gpu)
+    sc = oracle.index_scores(host_bits(q_i[rt].cpu()), host_bits(k_i.cpu()), w.cpu().numpy(),
+                             rows, p)
+    assert np.array_equal(idx[rt].cpu().numpy(), oracle.topk(sc, rows, p, k))
+    say("  idx bit-exact on %d sampled rows" % len(rows))
