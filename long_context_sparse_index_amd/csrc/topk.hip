@@ -33,6 +33,7 @@ constexpr int kBins0 = 4096;  // first digit: the top 12 bits of the key
 constexpr int kCand = 4096;   // candidate list: keys of the first digit's threshold bin
 constexpr int kLoads = 2;     // float4 loads in flight per thread while streaming a row
 constexpr int kSampleMinVis = 32768;  // rows at least this long take the sampled select
+constexpr int kPeelMax = 8;           // winners peeled off before a halved final sort
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t index) {
   return (static_cast<uint64_t>(~key) << 32) | index;  // ascending = key desc, index asc
@@ -259,6 +260,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
   __shared__ uint32_t pick[3];
   __shared__ uint32_t fill[3];  // slots taken in buf and in cand; sample size
   __shared__ uint32_t cand_max;  // largest key collected by the sampled path
+  __shared__ uint64_t peel_max[kTopkWaves];  // per-wave maxima while peeling the tail
+  __shared__ uint32_t peel_pos;
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -352,6 +355,48 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     }
   };
 
+  // Sorts the k winners in buf[0, k) ascending on (~key, pool).  When k is a little above a
+  // power of two (k = 2051 of the Flash shape), the k - 2^m worst winners are peeled off to
+  // the tail first, largest first, by block-wide maxima (three barriers each), so the
+  // bitonic network sorts 2^m keys instead of 2^(m+1).
+  auto sort_winners = [&]() {
+    int n2 = max(next_pow2(k), kTopkThreads);
+    int kk = k;
+    const int half = n2 >> 1;
+    if (n2 > kTopkThreads && k - half <= kPeelMax) {
+      const int lane = tid & 63;
+      __syncthreads();  // every winner is in buf
+      for (int m = k; m > half; --m) {  // the largest of buf[0, m) goes to buf[m - 1]
+        uint64_t v = 0ull;
+        for (int j = tid; j < m; j += kTopkThreads) v = buf[j] > v ? buf[j] : v;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          const uint64_t o = lane_xor_u64(v, off);
+          v = o > v ? o : v;
+        }
+        if (lane == 0) peel_max[tid >> 6] = v;
+        __syncthreads();
+        uint64_t gm = peel_max[0];
+#pragma unroll
+        for (int w = 1; w < kTopkWaves; ++w) gm = peel_max[w] > gm ? peel_max[w] : gm;
+        for (int j = tid; j < m; j += kTopkThreads)
+          if (buf[j] == gm) peel_pos = static_cast<uint32_t>(j);  // winners are distinct
+        __syncthreads();
+        if (tid == 0) {
+          const uint32_t pos = peel_pos;
+          buf[pos] = buf[m - 1];
+          buf[m - 1] = gm;
+        }
+        __syncthreads();
+      }
+      n2 = half;
+      kk = half;
+    }
+    for (int i = kk + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
+    __syncthreads();
+    sort_keys(buf, cand, n2);
+  };
+
   if constexpr (FROM_CAND) {
     // The list holds every visible entry whose key is >= the row's threshold (all visible
     // entries when the threshold is 0).  With at least k (or all vis <= k) and at most kCand
@@ -400,10 +445,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     int shift;
     digit_window(t_est, cand_max, &mask, &prefix, &shift);
     resolve_candidates(static_cast<int>(n), prefix, mask, k, shift);
-    const int n2 = max(next_pow2(k), kTopkThreads);
-    for (int i = k + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
-    __syncthreads();
-    sort_keys(buf, cand, n2);
+    sort_winners();
     for (int i = tid; i < k; i += kTopkThreads)
       orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
     return;
@@ -641,10 +683,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     }
   }
 
-  const int n2 = max(next_pow2(k), kTopkThreads);
-  for (int i = k + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
-  __syncthreads();
-  sort_keys(buf, cand, n2);
+  sort_winners();
   for (int i = tid; i < k; i += kTopkThreads)
     orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
 }

@@ -107,7 +107,7 @@ def _edge_scores(kind, nq, ld, rng):
 
 @pytest.mark.parametrize("kind", ["ties", "few_values", "signed_zero_neg", "normal",
                                   "clustered_ints"])
-@pytest.mark.parametrize("k", [1, 100, 2048, 2051, 4096])
+@pytest.mark.parametrize("k", [1, 100, 1030, 2048, 2051, 2056, 4096])
 def test_topk_edge_cases(gpu, kind, k):
     say("case: topk edge kind=%s k=%d" % (kind, k))
     rng = np.random.default_rng(zlib.crc32(("%s/%d" % (kind, k)).encode()))
