@@ -108,3 +108,51 @@ def test_chunked_rejects_small_workspace(lib):
                                  0, 8, 128, 128, 0.1, 256, 4096, 1024, 512, FAKE, 2, FAKE, None,
                                  P(0x100000), need - 1, None)
     assert st == 3
+
+
+def test_fused_select_and_deterministic_workspaces(lib):
+    # the fused select keeps a full score buffer for its exact redo, plus 32 KB of candidate
+    # list per row, a 1/16 sample of the scores and per-row flags
+    need = lib.dsa_index_topk_workspace_bytes(8192, 32768, 2048)
+    assert need >= 8192 * 32768 * 4 + 8192 * 4096 * 8 + 8192 * 2048 * 4
+    assert lib.dsa_index_topk_workspace_bytes(0, 32768, 2048) == 0
+    assert (lib.dsa_index_topk_workspace_bytes(100, 32768, 2048)
+            < lib.dsa_index_topk_workspace_bytes(200, 32768, 2048))
+    # the chunked forward holds the fused select's workspace and the index chunk
+    assert (lib.dsa_forward_chunked_workspace_bytes(32768, 8192, 2048)
+            >= lib.dsa_index_topk_workspace_bytes(8192, 32768, 2048) + 8192 * 2048 * 4)
+    # k above the fused select's limit: score chunk, index chunk and top-k workspace only
+    assert (lib.dsa_forward_chunked_workspace_bytes(32768, 8192, 3000)
+            < lib.dsa_index_topk_workspace_bytes(8192, 32768, 2048))
+    # deterministic backward: the per-row deltas plus 8 bytes per dK (and dV) element
+    base = lib.dsa_sparse_attn_bwd_workspace_bytes(100, 64)
+    det = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 576, 512, 0)
+    det_v = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 576, 512, 1)
+    assert det >= base + 5000 * 576 * 8
+    assert det_v - det == 5000 * 512 * 8
+
+
+def test_fused_select_and_deterministic_backward_reject_bad_arguments(lib):
+    it = lib.dsa_index_topk
+    # k beyond the fused select (2730), null idx, bad d_i, short or misaligned workspace
+    assert it(FAKE, 256, FAKE, 64, FAKE, 0, 0, 16, 1024, 4, 64, 0, 2731, FAKE, FAKE, 1 << 30,
+              None) == 2
+    assert it(FAKE, 256, FAKE, 64, FAKE, 0, 0, 16, 1024, 4, 64, 0, 256, None, FAKE, 1 << 30,
+              None) == 1
+    assert it(FAKE, 256, FAKE, 64, FAKE, 0, 0, 16, 1024, 4, 48, 0, 256, FAKE, FAKE, 1 << 30,
+              None) == 2
+    need = lib.dsa_index_topk_workspace_bytes(16, 1024, 256)
+    assert it(FAKE, 256, FAKE, 64, FAKE, 0, 0, 16, 1024, 4, 64, 0, 256, FAKE, P(0x100000),
+              need - 1, None) == 3
+    assert it(FAKE, 256, FAKE, 64, FAKE, 0, 0, 16, 1024, 4, 64, 0, 256, FAKE, P(0x100010),
+              need, None) == 3
+    det = lib.dsa_sparse_attn_bwd_deterministic
+    F32 = 2
+    # separate v without dv; (d_qk, d_v) without a kernel; short workspace
+    assert det(FAKE, FAKE, 576, FAKE, 512, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
+               4, 100, 64, 576, 512, 0.1, FAKE, 1 << 30, None) == 1
+    assert det(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None, 4,
+               100, 64, 576, 256, 0.1, FAKE, 1 << 30, None) == 2
+    need = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(4, 64, 100, 576, 512, 0)
+    assert det(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None, 4,
+               100, 64, 576, 512, 0.1, P(0x100000), need - 1, None) == 3
