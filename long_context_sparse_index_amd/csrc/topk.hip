@@ -402,6 +402,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     // entries when the threshold is 0).  With at least k (or all vis <= k) and at most kCand
     // of them it holds the k winners, resolved here as in the sampled path; any other count
     // leaves the row to the fallback (indexer scores + the score-row select).
+    // Every list has room for kCand entries: all of it is requested before the count
+    // arrives (entries past the count are ignored), so the loads take one round trip.
+    static_assert(kCand == 4 * kTopkThreads, "four list entries per thread");
+    const uint64_t* crow = cs.cand + r * cs.cap;
+    uint64_t pre[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pre[u] = crow[u * kTopkThreads + tid];
     const uint32_t n = cs.cnt[r];
     const bool usable = vis <= k ? n == static_cast<uint32_t>(vis)
                                  : (n >= static_cast<uint32_t>(k) &&
@@ -411,16 +418,15 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
       if (!usable) atomicOr(cs.any_fail, 1);
     }
     if (!usable) return;
-    const uint64_t* crow = cs.cand + r * cs.cap;
     if (vis <= k) {
       const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
-      for (int i = tid; i < n2; i += kTopkThreads) {
-        if (i < vis) {
-          const uint64_t c = crow[i];
-          buf[i] = composite(static_cast<uint32_t>(c >> 32), static_cast<uint32_t>(c));
-        } else {
-          buf[i] = ~0ull;
-        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = u * kTopkThreads + tid;
+        if (i < n2)
+          buf[i] = i < vis ? composite(static_cast<uint32_t>(pre[u] >> 32),
+                                       static_cast<uint32_t>(pre[u]))
+                           : ~0ull;
       }
       __syncthreads();
       sort_keys(buf, cand, n2);
@@ -432,11 +438,14 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     if (tid == 0) cand_max = 0u;
     __syncthreads();
     uint32_t my_max = 0u;
-    for (int i = tid; i < static_cast<int>(n); i += kTopkThreads) {
-      const uint64_t c = crow[i];
-      cand[i] = c;
-      const uint32_t key = static_cast<uint32_t>(c >> 32);
-      my_max = key > my_max ? key : my_max;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = u * kTopkThreads + tid;
+      if (i < static_cast<int>(n)) {
+        cand[i] = pre[u];
+        const uint32_t key = static_cast<uint32_t>(pre[u] >> 32);
+        my_max = key > my_max ? key : my_max;
+      }
     }
     if (my_max) atomicMax(&cand_max, my_max);
     __syncthreads();
