@@ -78,6 +78,32 @@ def test_indexer_fp8_bit_exact(gpu, h_i):
     _check_scores(scores, ref, rows, wl.n_pools)
 
 
+@pytest.mark.parametrize("d_i", [128, 256])
+def test_indexer_fp8_scaled_and_general_tiles(gpu, d_i):
+    """e4m3 query tiles whose head weights are all positive powers of two take the kernel
+    that folds the weight into the MFMA's B scale; the others the general epilogue.  One call
+    mixing both (a 3.0 weight, a zero weight, negative weights in some 32-row tiles) must be
+    bit-exact against the oracle on every row, the ragged last tile included."""
+    say("case: indexer fp8 scaled/general tiles, d_i=%d" % d_i)
+    rng = np.random.default_rng(17 + d_i)
+    nq, p, h_i, q_start = 200, 900, 8, 3000
+    x = rng.integers(-8, 9, size=(nq, h_i, d_i)).astype(np.float32)
+    y = rng.integers(-8, 9, size=(p, d_i)).astype(np.float32)
+    q = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).to(gpu)
+    k = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).to(gpu)
+    wh = np.tile(np.array([2.0 ** -(j % 4) for j in range(h_i)], np.float32), (nq, 1))
+    wh[70, 3] = 3.0      # tile 2: not a power of two
+    wh[100, 0] = 0.0     # tile 3: zero weight
+    wh[130:140, 5] = -0.5  # tile 4: negative weights
+    wh[199, 7] = 0.375   # the ragged last tile
+    w = torch.from_numpy(wh).to(gpu)
+    scores = B.index_scores_new(q, k, w, q_start=q_start)
+    torch.cuda.synchronize()
+    rows = np.arange(q_start, q_start + nq)
+    ref = oracle.index_scores(host_bits(q), host_bits(k), wh, rows, p)
+    _check_scores(scores, ref, rows, p)
+
+
 def test_topk_tiny_bit_exact(gpu):
     say("case: topk tiny_4k")
     q, k, w = I.index_inputs(TINY, gpu)
