@@ -104,6 +104,55 @@ def test_indexer_fp8_scaled_and_general_tiles(gpu, d_i):
     _check_scores(scores, ref, rows, p)
 
 
+@pytest.mark.parametrize("h_i,d_i,dtype", [(4, 128, "bf16"), (8, 128, "bf16"),
+                                          (16, 128, "bf16"), (8, 64, "bf16"), (8, 128, "fp8")])
+def test_indexer_large_launch_few_heads(gpu, h_i, d_i, dtype):
+    """Few heads over 131k pools in one launch of 1000 rows (thousands of blocks, both query
+    tile sizes): every visible score bit-identical to 32-row calls, nothing written past a
+    row's visible prefix, and the oracle's scores on rows at each position of 32- and 64-row
+    tiles, at the causal edge (pool count still growing) and at the ragged end.  Written in
+    one call and as a head split (write, then accumulate)."""
+    p, nq = 131072 + 77, 1000
+    q_start = 4 * p - 600  # local rows below 599 see fewer than p pools
+    say("case: indexer large launch h_i=%d d_i=%d %s (P=%d, nq=%d)" % (h_i, d_i, dtype, p,
+                                                                           nq))
+    rng = np.random.default_rng(1000 * h_i + d_i + (1 if dtype == "fp8" else 0))
+    r = 8 if dtype == "fp8" else 4
+
+    def ints(shape):
+        x = torch.from_numpy(rng.integers(-r, r + 1, size=shape).astype(np.float32))
+        x = x.to(torch.bfloat16) if dtype == "bf16" else x.to(torch.float8_e4m3fn).view(
+            torch.uint8)
+        return x.to(gpu)
+
+    q, k = ints((nq, h_i, d_i)), ints((p, d_i))
+    # per-row weights in eighths, zero and negative ones included: every score stays exact
+    w = torch.from_numpy((rng.integers(-8, 17, size=(nq, h_i)) / 8.0).astype(np.float32)).to(gpu)
+    ld = ((p + 3) // 4) * 4
+    one = torch.full((nq, ld), float("nan"), device=gpu)
+    B.index_scores(q, k, w, one, q_start=q_start)
+    split = torch.full((nq, ld), float("nan"), device=gpu)
+    h0 = h_i // 2
+    B.index_scores(q[:, :h0], k, w[:, :h0], split, q_start=q_start)
+    B.index_scores(q[:, h0:], k, w[:, h0:], split, q_start=q_start, accumulate=True)
+    ref = torch.full((nq, ld), float("nan"), device=gpu)
+    for r0 in range(0, nq, 32):
+        r1 = min(nq, r0 + 32)
+        B.index_scores(q[r0:r1], k, w[r0:r1], ref[r0:r1], q_start=q_start + r0)
+    torch.cuda.synchronize()
+    t = torch.arange(q_start, q_start + nq, device=gpu, dtype=torch.int64)
+    vis = torch.clamp((t + 1) // 4, max=p)
+    inside = torch.arange(ld, device=gpu)[None, :] < vis[:, None]
+    assert bool(torch.isnan(ref[~inside]).all())
+    for name, got in (("one call", one), ("head split", split)):
+        assert torch.equal(got[inside].view(torch.int32), ref[inside].view(torch.int32)), name
+        assert bool(torch.isnan(got[~inside]).all()), name + " wrote past a visible prefix"
+    rows = np.array([0, 31, 32, 63, 64, 95, 96, 127, 128, 598, 599, 600, 960, 999])
+    want = oracle.index_scores(host_bits(q[torch.from_numpy(rows).to(gpu)]), host_bits(k),
+                               w.cpu().numpy()[rows], q_start + rows, p)
+    _check_scores(one[torch.from_numpy(rows).to(gpu)], want, q_start + rows, p)
+
+
 def test_topk_tiny_bit_exact(gpu):
     say("case: topk tiny_4k")
     q, k, w = I.index_inputs(TINY, gpu)

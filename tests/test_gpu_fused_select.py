@@ -64,6 +64,8 @@ CASES = [
     ("d32_k1", 9000, 12, 32, "bf16", 1, 30000, 77),
     ("k2730", 30000, 5, 64, "bf16", 2730, 4 * 30000 - 50, 100),
     ("boundary_4096", 8192, 4, 64, "bf16", 2048, 4 * 4096 - 40, 80),
+    # 8 heads over 131k pools: a candidate pass of thousands of blocks
+    ("large_131k_8h", 131149, 8, 128, "bf16", 2048, 4 * 131149 - 600, 1000),
 ]
 
 
