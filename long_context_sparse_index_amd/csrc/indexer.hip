@@ -187,6 +187,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const int row = i - j * kBQ;
     w_lds[i] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
   }
+  // Candidate counters of the tile's rows: past the weights when they leave room, zeroed
+  // here (the head loop's barriers order this before the epilogue's LDS atomics), else on
+  // the weights once the last head has read them.
+  const bool counters_apart = h_i <= kMaxHeads - 2;
+  if constexpr (EMIT) {
+    if (counters_apart && tid < kBQ) reinterpret_cast<uint32_t*>(w_lds)[h_i * kBQ + tid] = 0u;
+  }
 
   // This wave's pooled key rows, resident for all heads.
   Frag kf[kMB][kKS];
@@ -295,15 +302,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     // score is >= the threshold's float (one compare each; a threshold key of 0 takes every
     // finite score).  Each lane marks its candidates in a bit mask per row, takes its offset
     // in the tile's share of the row with one LDS atomic, one thread per row reserves that
-    // share in the row's list, and the marked entries are written.  The counters reuse the
-    // head weights' LDS once every wave is past the loop.
+    // share in the row's list, and the marked entries are written.
     static_assert(2 * kBQ <= kBQ * kMaxHeads, "counters fit the weight array");
     static_assert(kMB * 4 <= 32, "one 32-bit mask per row");
-    uint32_t* const c_cnt = reinterpret_cast<uint32_t*>(w_lds);
+    uint32_t* const c_cnt = reinterpret_cast<uint32_t*>(w_lds) + (counters_apart ? h_i * kBQ : 0);
     uint32_t* const c_base = c_cnt + kBQ;
-    __syncthreads();
-    if (tid < kBQ) c_cnt[tid] = 0u;
-    __syncthreads();
+    if (!counters_apart) {
+      __syncthreads();
+      if (tid < kBQ) c_cnt[tid] = 0u;
+      __syncthreads();
+    }
     uint32_t mask[NB], off[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
