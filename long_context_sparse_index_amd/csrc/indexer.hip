@@ -14,11 +14,13 @@
 // the per-head products never leave the register file.  Products are laid out
 // pool-major (MFMA rows = pools, columns = queries), which puts one query per lane column:
 // the head weight is one value per lane and the finished scores go out as 16-byte rows.
+// With few heads a block keeps its key rows for several consecutive query tiles, the
+// staging running on from one tile's last head to the next tile's first.
 //
 // The grid covers the causal trapezoid: tiles whose first pool lies beyond the visible
 // prefix of the tile's last query exit at once.  Block ids are remapped so that the pool
-// tiles of one query tile run on the same XCD (blocks are dealt to the 8 XCDs round-robin)
-// and share the query tile through that XCD's L2.
+// tiles of one query tile (or group of tiles) run on the same XCD (blocks are dealt to the
+// 8 XCDs round-robin) and share the queries through that XCD's L2.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -32,6 +34,11 @@ constexpr int kPoolsPerWave = 64;
 constexpr int kMB = kPoolsPerWave / 16;
 constexpr int kPoolsPerBlock = kIdxWaves * kPoolsPerWave;
 constexpr int kMaxHeads = 64;
+// Few-head score launches: (query tile, head) passes per block's key-row load at most, and
+// the grid size below which blocks take fewer query tiles.
+constexpr int kPassesPerKeyLoad = 32;
+constexpr int kMinBlocks = 2048;
+static_assert(kPassesPerKeyLoad <= kMaxHeads, "the passes' weights fit the weight array");
 
 template <bool FP8>
 struct FragT;
@@ -99,13 +106,15 @@ __device__ __forceinline__ void idx_dma_16b(const void* src, uint32_t lds_addr) 
 
 // D: d_i; NB: 16-query column blocks per tile (BQ = 16 * NB); FP8: e4m3 operands; EMIT:
 // instead of storing scores, append the (key, pool) pairs whose order key reaches the row's
-// threshold to the row's candidate list (IndexerOpts).
-template <int D, int NB, bool FP8, bool EMIT>
+// threshold to the row's candidate list (IndexerOpts); MULTI: a block takes group_tiles
+// consecutive query tiles (else one).
+template <int D, int NB, bool FP8, bool EMIT, bool MULTI>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const uint8_t* __restrict__ q, int64_t q_stride_b, const uint8_t* __restrict__ k,
     int64_t k_stride_b, const float* __restrict__ w, int64_t w_stride,
     float* __restrict__ scores, int64_t ld, int64_t q_start, int64_t nq, int64_t n_pools,
-    int h_i, int accumulate, int n_pool_tiles, int n_query_tiles, IndexerOpts opt) {
+    int h_i, int accumulate, int n_pool_tiles, int n_query_groups, int group_tiles,
+    IndexerOpts opt) {
   using Frag = typename FragT<FP8>::type;
   constexpr int kRowBytes = D * (FP8 ? 1 : 2);
   constexpr int kFragBytes = FP8 ? 32 : 16;        // bytes of one row per lane group
@@ -135,6 +144,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   };
 
   if (opt.gate && *opt.gate == 0) return;  // gated launch with nothing to do
+  static_assert(!(EMIT && MULTI), "the candidate pass takes one query tile per block");
   // With pool_shift s the key table is read at every 2^s-th pool (the caller scales the key
   // stride): column c is pool c * 2^s, visible to t iff c * 2^s < V(t).
   const int sh = opt.pool_shift;
@@ -142,18 +152,39 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     return (visible_pools(t, n_pools) + (int64_t{1} << sh) - 1) >> sh;
   };
   const int64_t n_cols = (n_pools + (int64_t{1} << sh) - 1) >> sh;
-  // XCD-aware remap: consecutive logical tiles (same query tile) land on one XCD.
-  const int n_tiles = n_pool_tiles * n_query_tiles;
+  // XCD-aware remap: consecutive logical tiles (same query group) land on one XCD.
+  const int n_tiles = n_pool_tiles * n_query_groups;
   const int per_xcd = (n_tiles + 7) >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= n_tiles) return;
-  const int qt = logical / n_pool_tiles;
-  const int pt = logical - qt * n_pool_tiles;
-  const int64_t q0 = static_cast<int64_t>(qt) * kBQ;
+  const int qg = logical / n_pool_tiles;
+  const int pt = logical - qg * n_pool_tiles;
   const int64_t p0 = static_cast<int64_t>(pt) * kPoolsPerBlock;
-  const int64_t rows_here = (nq - q0) < kBQ ? (nq - q0) : kBQ;
-  const int64_t vis_last = vis_of(q_start + q0 + rows_here - 1);
-  if (p0 >= vis_last) return;  // whole tile above the causal boundary
+  // The block's query tiles [qt_first, qt_first + n_qt): tile qg alone, or (MULTI) the
+  // tiles of group qg that see some of the block's pools.  Visible prefixes grow with the
+  // query, so the tiles that see none come first and are skipped.
+  auto vis_last_of = [&](int64_t qt) {  // visible columns of the tile's last row
+    const int64_t last = (qt + 1) * kBQ < nq ? (qt + 1) * kBQ - 1 : nq - 1;
+    return vis_of(q_start + last);
+  };
+  int64_t qt_first = qg;
+  int n_qt = 1;
+  if constexpr (MULTI) {
+    const int64_t n_query_tiles = (nq + kBQ - 1) / kBQ;
+    const int64_t qt_end = (static_cast<int64_t>(qg) + 1) * group_tiles < n_query_tiles
+                               ? (static_cast<int64_t>(qg) + 1) * group_tiles
+                               : n_query_tiles;
+    if (p0 >= vis_last_of(qt_end - 1)) return;  // every tile above the causal boundary
+    qt_first = static_cast<int64_t>(qg) * group_tiles;
+    while (p0 >= vis_last_of(qt_first)) ++qt_first;  // stops at qt_end - 1 at the latest
+    n_qt = static_cast<int>(qt_end - qt_first);
+  }
+  // Visible columns of the block's last row.
+  const int64_t vis_last = vis_last_of(qt_first + n_qt - 1);
+  if constexpr (!MULTI) {
+    if (p0 >= vis_last) return;  // whole tile above the causal boundary
+  }
+  const int n_pass = n_qt * h_i;  // (query tile, head) passes, head-minor
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -161,12 +192,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int64_t pw0 = p0 + wid * kPoolsPerWave;
-  const bool wave_live = pw0 < vis_last;
+  // The wave's pools are visible to some row of the block (its last row).
+  const bool keys_live = pw0 < vis_last;
 
   if (opt.gate_rows) {
-    // Only query tiles holding a flagged row: wave 0 checks the tile's rows (kBQ <= 64) and
-    // passes the verdict through the weight array's first word before the weights land.
+    // Only query tiles holding a flagged row (one tile per block here): wave 0 checks the
+    // tile's rows (kBQ <= 64) and passes the verdict through the weight array's first word
+    // before the weights land.
     static_assert(kBQ <= kWave, "one wave checks the tile");
+    const int64_t q0 = qt_first * kBQ;
     uint32_t* const verdict = reinterpret_cast<uint32_t*>(w_lds);
     if (tid < kWave) {
       const bool flagged = tid < kBQ && q0 + tid < nq && opt.gate_rows[q0 + tid] != 0;
@@ -179,13 +213,17 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     if (!any_row) return;
   }
 
-  // Head weights of the tile's queries, stored [head][query] so that the 16 lanes of a group
-  // read 16 consecutive words; consecutive threads write consecutive words (walking the
-  // rows of one head first avoids 32-way bank conflicts on the transposing stores).
-  for (int i = tid; i < kBQ * h_i; i += kIdxThreads) {
-    const int j = i / kBQ;
-    const int row = i - j * kBQ;
-    w_lds[i] = (q0 + row < nq) ? w[(q0 + row) * w_stride + j] : 0.0f;
+  // Head weights of the block's queries, pass-major ([tile][head][query]) so that the 16
+  // lanes of a group read 16 consecutive words; consecutive threads write consecutive words
+  // (walking the rows of one head first avoids 32-way bank conflicts on the transposing
+  // stores).  The host keeps n_qt * h_i <= kMaxHeads.
+  for (int i = tid; i < n_pass * kBQ; i += kIdxThreads) {
+    const int jj = i / kBQ;
+    const int row = i - jj * kBQ;
+    const int qi = MULTI ? jj / h_i : 0;
+    const int j = jj - qi * h_i;
+    const int64_t t = (qt_first + qi) * kBQ + row;
+    w_lds[i] = t < nq ? w[t * w_stride + j] : 0.0f;
   }
   // Candidate counters of the tile's rows: past the weights when they leave room, zeroed
   // here (the head loop's barriers order this before the epilogue's LDS atomics), else on
@@ -195,249 +233,309 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     if (counters_apart && tid < kBQ) reinterpret_cast<uint32_t*>(w_lds)[h_i * kBQ + tid] = 0u;
   }
 
-  // This wave's pooled key rows, resident for all heads.
+  // This wave's pooled key rows, resident for all of the block's passes.
   Frag kf[kMB][kKS];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
     const int64_t pool = pw0 + mb * 16 + r16;
-    const bool ok = wave_live && pool < n_cols;
+    const bool ok = keys_live && pool < n_cols;
     const uint8_t* kp = k + (ok ? pool : 0) * k_stride_b + g * kFragBytes;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
       kf[mb][ks] = ok ? load_frag<FP8>(kp + ks * kStepBytes) : zero_frag<FP8>();
   }
 
-  // This lane's source rows for the query-tile loads: the wave's load i is the head's 1 KB
-  // load L = wid + 4 i (if L < kDmaPerHead); lane slot s = 64 L + lane -> row s / kCpr,
-  // position s % kCpr.
+  // This lane's share of a pass's query-tile loads: the wave's load i is the pass's 1 KB load
+  // L = wid + 4 i (if L < kDmaPerHead); lane slot s = 64 L + lane -> row s / kCpr, position
+  // s % kCpr.
+  // One tile: the loads' source rows are fixed, so their addresses are formed once.
+  int dma_row[kDmaPerWave];
+  int dma_chunk[kDmaPerWave];
   const uint8_t* dma_src[kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
     const int slot = 64 * (wid + kIdxWaves * i) + lane;
     const int row = (slot / kCpr) % kBQ;  // loads past the tile (not issued) stay in range
-    const int chunk = (slot % kCpr) ^ swz(row);
-    const int64_t qrow = q0 + row < nq ? q0 + row : nq - 1;  // rows past nq: any valid row
-    dma_src[i] = q + qrow * q_stride_b + chunk * 16;
+    dma_row[i] = row;
+    dma_chunk[i] = (slot % kCpr) ^ swz(row);
+    const int64_t t = qt_first * kBQ + row;
+    dma_src[i] = q + (t < nq ? t : nq - 1) * q_stride_b + dma_chunk[i] * 16;  // any valid row
   }
   const uint32_t q_lds_a = lds_addr_of(q_lds);
-  auto issue = [&](int j) {
+  auto issue = [&](int jj) {
+    const int qi = MULTI ? jj / h_i : 0;
+    const int j = jj - qi * h_i;
+    const int64_t t0 = (qt_first + qi) * kBQ;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i)
-      if (wid + kIdxWaves * i < kDmaPerHead)
-        idx_dma_16b(dma_src[i] + static_cast<int64_t>(j) * kRowBytes,
-                    q_lds_a + (j % kStages) * kHeadBytes + (wid + kIdxWaves * i) * 1024);
+      if (wid + kIdxWaves * i < kDmaPerHead) {
+        const uint32_t dst = q_lds_a + (jj % kStages) * kHeadBytes + (wid + kIdxWaves * i) * 1024;
+        if constexpr (MULTI) {
+          const int64_t t = t0 + dma_row[i];
+          idx_dma_16b(q + (t < nq ? t : nq - 1) * q_stride_b + j * kRowBytes + dma_chunk[i] * 16,
+                      dst);
+        } else {
+          idx_dma_16b(dma_src[i] + static_cast<int64_t>(j) * kRowBytes, dst);
+        }
+      }
   };
 
   f32x4 sc[kMB][NB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int j = 0; j < kStages - 1 && j < h_i; ++j) issue(j);
-  // The key rows and the first heads' loads land together.  Waiting for them here, once,
-  // also tells the compiler that the key registers are complete before the head loop;
-  // otherwise it would wait for every outstanding load (the prefetched heads included) at
+  for (int jj = 0; jj < kStages - 1 && jj < n_pass; ++jj) issue(jj);
+  // The key rows and the first passes' loads land together.  Waiting for them here, once,
+  // also tells the compiler that the key registers are complete before the pass loop;
+  // otherwise it would wait for every outstanding load (the prefetched passes included) at
   // their first use in each iteration.
   IDX_WAIT_VMCNT(0);
   // B-operand rows of this lane: query nb * 16 + r16 of the tile.
   const lds_ptr qb = lds_ptr_of(q_lds);
-  for (int j = 0; j < h_i; ++j) {
-    // Head j's loads (and the key rows before them) have landed for this wave.
-    const int ahead = h_i - 1 - j < kStages - 2 ? h_i - 1 - j : kStages - 2;
-    if (ahead >= 2) {
-      IDX_WAIT_VMCNT(2 * kDmaPerWave);
-    } else if (ahead == 1) {
-      IDX_WAIT_VMCNT(kDmaPerWave);
-    } else {
-      IDX_WAIT_VMCNT(0);
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // head j's tile is in LDS for every wave; j - 1 consumed
-    asm volatile("" ::: "memory");
-    if (j + kStages - 1 < h_i) issue(j + kStages - 1);
-    if (wave_live) {
-      const lds_ptr stage = qb + (j % kStages) * kHeadBytes;
-      f32x4 acc[kMB][NB];
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int64_t q0 = (qt_first + qi) * kBQ;
+    const bool wave_live = MULTI ? pw0 < vis_last_of(qt_first + qi) : keys_live;
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        Frag qf[NB];
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = qi * h_i; jj < (qi + 1) * h_i; ++jj) {
+      // Pass jj's loads (and the key rows before them) have landed for this wave.  A
+      // finished tile's score stores are younger than some of the loads waited for, so
+      // those waits also wait for them (the counter counts in order).
+      const int ahead = n_pass - 1 - jj < kStages - 2 ? n_pass - 1 - jj : kStages - 2;
+      if (ahead >= 2) {
+        IDX_WAIT_VMCNT(2 * kDmaPerWave);
+      } else if (ahead == 1) {
+        IDX_WAIT_VMCNT(kDmaPerWave);
+      } else {
+        IDX_WAIT_VMCNT(0);
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // pass jj's tile is in LDS for every wave; jj - 1 read
+      asm volatile("" ::: "memory");
+      if (jj + kStages - 1 < n_pass) issue(jj + kStages - 1);
+      if (wave_live) {
+        const lds_ptr stage = qb + (jj % kStages) * kHeadBytes;
+        f32x4 acc[kMB][NB];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          Frag qf[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int row = nb * 16 + r16;
+            const int c0 = (ks * kStepBytes + g * kFragBytes) / 16;
+            if constexpr (FP8) {
+              const u32x4 lo =
+                  *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                      stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+              const u32x4 hi =
+                  *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                      stage + row * kRowBytes + (((c0 + 1) ^ swz(row)) * 16));
+              for (int e = 0; e < 4; ++e) {
+                qf[nb][e] = lo[e];
+                qf[nb][4 + e] = hi[e];
+              }
+            } else {
+              qf[nb] = lds_load_bf16x8(stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+            }
+          }
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)  // the first step starts from a literal zero
+              acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
+                                           ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const int row = nb * 16 + r16;
-          const int c0 = (ks * kStepBytes + g * kFragBytes) / 16;
-          if constexpr (FP8) {
-            const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
-            const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                stage + row * kRowBytes + (((c0 + 1) ^ swz(row)) * 16));
-            for (int e = 0; e < 4; ++e) {
-              qf[nb][e] = lo[e];
-              qf[nb][4 + e] = hi[e];
-            }
-          } else {
-            qf[nb] = lds_load_bf16x8(stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
-          }
+          const float wv = w_lds[jj * kBQ + nb * 16 + r16];
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
         }
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)  // the first step starts from a literal zero
-            acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
-                                         ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
       }
+    }
+    // The tile's scores are complete.  With several tiles per block, the lane coordinates
+    // pass through an empty asm statement first, so that no address or bound of the
+    // epilogue (all invariant across tiles) is computed before the tile loop and held in
+    // registers through it (that costs a wave per SIMD).
+    int r16e = r16, ge = g;
+    int64_t pw0e = pw0;
+    if constexpr (MULTI) asm volatile("" : "+v"(r16e), "+v"(ge), "+s"(pw0e));
+    if constexpr (EMIT) {
+      // Candidates: visible entries whose order key reaches the row's threshold, i.e. whose
+      // score is >= the threshold's float (one compare each; a threshold key of 0 takes
+      // every finite score).  Each lane marks its candidates in a bit mask per row, takes
+      // its offset in the tile's share of the row with one LDS atomic, one thread per row
+      // reserves that share in the row's list, and the marked entries are written.
+      static_assert(2 * kBQ <= kBQ * kMaxHeads, "counters fit the weight array");
+      static_assert(kMB * 4 <= 32, "one 32-bit mask per row");
+      uint32_t* const c_cnt =
+          reinterpret_cast<uint32_t*>(w_lds) + (counters_apart ? h_i * kBQ : 0);
+      uint32_t* const c_base = c_cnt + kBQ;
+      if (!counters_apart) {
+        __syncthreads();
+        if (tid < kBQ) c_cnt[tid] = 0u;
+        __syncthreads();
+      }
+      uint32_t mask[NB], off[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float wv = w_lds[j * kBQ + nb * 16 + r16];
+        const int64_t row = q0 + nb * 16 + r16e;
+        const bool live = wave_live && row < nq;
+        const int64_t vis = live ? vis_of(q_start + row) : 0;
+        const uint32_t tk = live ? opt.t_est[row] : 0u;
+        // float at the lower edge of the threshold key (keys with the top bit set are the
+        // non-negative floats)
+        const float thr =
+            tk == 0u ? -__builtin_inff()
+                     : __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
+        uint32_t m = 0u;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
+            m |= sc[mb][nb][i] >= thr ? (1u << (mb * 4 + i)) : 0u;
+        if (pw0e + kPoolsPerWave > vis) {  // tile on the causal boundary: drop invisible pools
+          const int64_t lim = vis - (pw0e + ge * 4);  // lane's pools: pw0 + g*4 + 16 mb + i
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (mb * 16 + i >= lim) m &= ~(1u << (mb * 4 + i));
+        }
+        mask[nb] = m;
+        off[nb] = m ? atomicAdd(&c_cnt[nb * 16 + r16e],
+                                static_cast<uint32_t>(__builtin_popcount(m)))
+                    : 0u;
       }
-    }
-  }
-  if constexpr (EMIT) {
-    // Candidates: visible entries whose order key reaches the row's threshold, i.e. whose
-    // score is >= the threshold's float (one compare each; a threshold key of 0 takes every
-    // finite score).  Each lane marks its candidates in a bit mask per row, takes its offset
-    // in the tile's share of the row with one LDS atomic, one thread per row reserves that
-    // share in the row's list, and the marked entries are written.
-    static_assert(2 * kBQ <= kBQ * kMaxHeads, "counters fit the weight array");
-    static_assert(kMB * 4 <= 32, "one 32-bit mask per row");
-    uint32_t* const c_cnt = reinterpret_cast<uint32_t*>(w_lds) + (counters_apart ? h_i * kBQ : 0);
-    uint32_t* const c_base = c_cnt + kBQ;
-    if (!counters_apart) {
       __syncthreads();
-      if (tid < kBQ) c_cnt[tid] = 0u;
-      __syncthreads();
-    }
-    uint32_t mask[NB], off[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int64_t row = q0 + nb * 16 + r16;
-      const bool live = wave_live && row < nq;
-      const int64_t vis = live ? vis_of(q_start + row) : 0;
-      const uint32_t tk = live ? opt.t_est[row] : 0u;
-      // float at the lower edge of the threshold key (keys with the top bit set are the
-      // non-negative floats)
-      const float thr = tk == 0u ? -__builtin_inff()
-                                 : __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
-      uint32_t m = 0u;
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          m |= sc[mb][nb][i] >= thr ? (1u << (mb * 4 + i)) : 0u;
-      if (pw0 + kPoolsPerWave > vis) {  // tile on the causal boundary: drop invisible pools
-        const int64_t lim = vis - (pw0 + g * 4);  // this lane's pools are pw0 + g*4 + 16 mb + i
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (mb * 16 + i >= lim) m &= ~(1u << (mb * 4 + i));
+      if (tid < kBQ && q0 + tid < nq) {
+        const uint32_t c = c_cnt[tid];
+        c_base[tid] = c ? atomicAdd(&opt.cand_cnt[q0 + tid], c) : 0u;
       }
-      mask[nb] = m;
-      off[nb] = m ? atomicAdd(&c_cnt[nb * 16 + r16], static_cast<uint32_t>(__builtin_popcount(m)))
-                  : 0u;
-    }
-    __syncthreads();
-    if (tid < kBQ && q0 + tid < nq) {
-      const uint32_t c = c_cnt[tid];
-      c_base[tid] = c ? atomicAdd(&opt.cand_cnt[q0 + tid], c) : 0u;
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (!mask[nb]) continue;
-      const int64_t row = q0 + nb * 16 + r16;
-      uint32_t slot = c_base[nb * 16 + r16] + off[nb];
-      uint64_t* const dst = opt.cand + row * opt.cand_cap;
+      for (int nb = 0; nb < NB; ++nb) {
+        if (!mask[nb]) continue;
+        const int64_t row = q0 + nb * 16 + r16e;
+        uint32_t slot = c_base[nb * 16 + r16e] + off[nb];
+        uint64_t* const dst = opt.cand + row * opt.cand_cap;
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        if (!((mask[nb] >> (mb * 4)) & 0xFu)) continue;
+        for (int mb = 0; mb < kMB; ++mb) {
+          if (!((mask[nb] >> (mb * 4)) & 0xFu)) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (mask[nb] & (1u << (mb * 4 + i))) {
-            if (slot < static_cast<uint32_t>(opt.cand_cap))
-              dst[slot] = (static_cast<uint64_t>(float_order_key(sc[mb][nb][i])) << 32) |
-                          static_cast<uint32_t>(pw0 + mb * 16 + g * 4 + i);
-            ++slot;
+          for (int i = 0; i < 4; ++i) {
+            if (mask[nb] & (1u << (mb * 4 + i))) {
+              if (slot < static_cast<uint32_t>(opt.cand_cap))
+                dst[slot] = (static_cast<uint64_t>(float_order_key(sc[mb][nb][i])) << 32) |
+                            static_cast<uint32_t>(pw0e + mb * 16 + ge * 4 + i);
+              ++slot;
+            }
           }
         }
       }
-    }
-    return;
-  }
-  if (!wave_live) return;
-
+    } else if (wave_live) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int64_t row = q0 + nb * 16 + r16;
-    if (row >= nq) continue;
-    const int64_t vis = vis_of(q_start + row);
-    float* dst_row = scores + row * ld;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = q0 + nb * 16 + r16e;
+        if (row >= nq) continue;
+        const int64_t vis = vis_of(q_start + row);
+        float* dst_row = scores + row * ld;
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int64_t p = pw0 + mb * 16 + g * 4;
-      f32x4 val = sc[mb][nb];
-      float* dst = dst_row + p;
-      if (p + 4 <= vis) {
-        if (accumulate) val += *reinterpret_cast<const f32x4*>(dst);
-        *reinterpret_cast<f32x4*>(dst) = val;
-      } else {
+        for (int mb = 0; mb < kMB; ++mb) {
+          const int64_t p = pw0e + mb * 16 + ge * 4;
+          f32x4 val = sc[mb][nb];
+          float* dst = dst_row + p;
+          if (p + 4 <= vis) {
+            if (accumulate) val += *reinterpret_cast<const f32x4*>(dst);
+            *reinterpret_cast<f32x4*>(dst) = val;
+          } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (p + i < vis) dst[i] = accumulate ? dst[i] + val[i] : val[i];
+            for (int i = 0; i < 4; ++i)
+              if (p + i < vis) dst[i] = accumulate ? dst[i] + val[i] : val[i];
+          }
+        }
       }
     }
   }
 }
 
-template <int D, int NB, bool FP8>
+template <int D, int NB, bool FP8, bool MULTI>
 hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
                              int64_t k_row_stride, const float* w, int64_t w_row_stride,
                              float* scores, int64_t ld, int64_t q_start, int64_t nq,
                              int64_t n_pools, int h_i, int accumulate, const IndexerOpts& opt,
+                             int64_t n_query_tiles, int64_t n_pool_tiles, int group_tiles,
                              hipStream_t stream) {
-  constexpr int kBQ = 16 * NB;
   const int64_t elt = FP8 ? 1 : 2;
   const int64_t step = int64_t{1} << opt.pool_shift;
-  const int64_t vis_pools = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
-  const int64_t vis_max = (vis_pools + step - 1) / step;
-  if (nq <= 0 || vis_max <= 0) return hipSuccess;
-  const int64_t n_query_tiles = (nq + kBQ - 1) / kBQ;
-  const int64_t n_pool_tiles = (vis_max + kPoolsPerBlock - 1) / kPoolsPerBlock;
-  const int64_t n_tiles = n_query_tiles * n_pool_tiles;
+  const int64_t n_query_groups = (n_query_tiles + group_tiles - 1) / group_tiles;
+  const int64_t n_tiles = n_query_groups * n_pool_tiles;
   if (n_tiles >= (int64_t{1} << 31) - 8) return hipErrorInvalidConfiguration;
   const int64_t grid = ((n_tiles + 7) / 8) * 8;
-  auto kern = opt.cand ? indexer_kernel<D, NB, FP8, true> : indexer_kernel<D, NB, FP8, false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kIdxThreads), 0, stream,
-                     static_cast<const uint8_t*>(q), q_row_stride * elt,
-                     static_cast<const uint8_t*>(k), k_row_stride * elt * step, w,
-                     w_row_stride, scores, ld, q_start, nq, n_pools, h_i, accumulate,
-                     static_cast<int>(n_pool_tiles), static_cast<int>(n_query_tiles), opt);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kIdxThreads), 0, stream,
+                       static_cast<const uint8_t*>(q), q_row_stride * elt,
+                       static_cast<const uint8_t*>(k), k_row_stride * elt * step, w,
+                       w_row_stride, scores, ld, q_start, nq, n_pools, h_i, accumulate,
+                       static_cast<int>(n_pool_tiles), static_cast<int>(n_query_groups),
+                       group_tiles, opt);
+  };
+  if constexpr (MULTI) {
+    args(indexer_kernel<D, NB, FP8, false, true>);
+  } else {
+    if (opt.cand)
+      args(indexer_kernel<D, NB, FP8, true, false>);
+    else
+      args(indexer_kernel<D, NB, FP8, false, false>);
+  }
   return hipGetLastError();
 }
 
-// Query tile of 32 rows, or of 64 rows when few heads (at most 8) leave each block little
-// MFMA work per key-row load: the larger tile doubles the queries each key row serves
-// (measured 5% faster at 8 heads, 3% slower at 32).  The 64-row tile is kept to d_i <= 128,
-// whose key, score and product registers still fit.
+// Tiles.  With few heads a block's key rows serve little MFMA work per load, so for score
+// output a block walks several consecutive 32-row query tiles (MULTI) with its key rows
+// resident and the query staging running on across tiles: up to kPassesPerKeyLoad (tile,
+// head) passes per key load, fewer tiles while the grid would hold fewer than kMinBlocks
+// blocks (measured 5-6% faster than 64-row single tiles at 8 heads).  Otherwise a block owns
+// one tile of 32 rows, or of 64 rows when few heads (at most 8) leave each block little MFMA
+// work per key-row load: the larger tile doubles the queries each key row serves (5% faster
+// at 8 heads, 3% slower at 32).  The 64-row tile and MULTI are kept to d_i <= 128, whose
+// key, score and product registers still fit.  The candidate pass (its epilogue holds more
+// registers across a tile loop), the sampled pass of the fused select (1% slower with tile
+// groups) and launches that compute only flagged tiles take single tiles.
 template <int D, bool FP8>
 hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
                             int64_t k_row_stride, const float* w, int64_t w_row_stride,
                             float* scores, int64_t ld, int64_t q_start, int64_t nq,
                             int64_t n_pools, int h_i, int accumulate, const IndexerOpts& opt,
                             hipStream_t stream) {
+  const int64_t step = int64_t{1} << opt.pool_shift;
+  const int64_t vis_pools = n_pools < (q_start + nq) / 4 ? n_pools : (q_start + nq) / 4;
+  const int64_t vis_max = (vis_pools + step - 1) / step;
+  if (nq <= 0 || vis_max <= 0) return hipSuccess;
+  const int64_t n_pool_tiles = (vis_max + kPoolsPerBlock - 1) / kPoolsPerBlock;
+  const int64_t tiles32 = (nq + 31) / 32;
   if constexpr (D <= 128) {
+    const bool single = opt.gate_rows || opt.cand || opt.pool_shift != 0;
+    int group_tiles = (single || h_i >= kPassesPerKeyLoad) ? 1 : kPassesPerKeyLoad / h_i;
+    while (group_tiles > 1 &&
+           ((tiles32 + group_tiles - 1) / group_tiles) * n_pool_tiles < kMinBlocks)
+      group_tiles /= 2;
+    if (group_tiles > 1)
+      return launch_indexer_nb<D, 2, FP8, true>(q, q_row_stride, k, k_row_stride, w,
+                                                w_row_stride, scores, ld, q_start, nq, n_pools,
+                                                h_i, accumulate, opt, tiles32, n_pool_tiles,
+                                                group_tiles, stream);
     if (h_i <= 8)
-      return launch_indexer_nb<D, 4, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
-                                          scores, ld, q_start, nq, n_pools, h_i, accumulate,
-                                          opt, stream);
+      return launch_indexer_nb<D, 4, FP8, false>(q, q_row_stride, k, k_row_stride, w,
+                                                 w_row_stride, scores, ld, q_start, nq, n_pools,
+                                                 h_i, accumulate, opt, (nq + 63) / 64,
+                                                 n_pool_tiles, 1, stream);
   }
-  return launch_indexer_nb<D, 2, FP8>(q, q_row_stride, k, k_row_stride, w, w_row_stride, scores,
-                                      ld, q_start, nq, n_pools, h_i, accumulate, opt, stream);
+  return launch_indexer_nb<D, 2, FP8, false>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
+                                             scores, ld, q_start, nq, n_pools, h_i, accumulate,
+                                             opt, tiles32, n_pool_tiles, 1, stream);
 }
 
 }  // namespace
