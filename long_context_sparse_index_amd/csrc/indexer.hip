@@ -34,11 +34,11 @@ constexpr int kPoolsPerWave = 64;
 constexpr int kMB = kPoolsPerWave / 16;
 constexpr int kPoolsPerBlock = kIdxWaves * kPoolsPerWave;
 constexpr int kMaxHeads = 64;
-// Few-head score launches: (query tile, head) passes per block's key-row load at most, and
-// the grid size below which blocks take fewer query tiles.
-constexpr int kPassesPerKeyLoad = 32;
+// Few-head score launches (at most kMaxGroupHeads heads): (query tile, head) passes per
+// block's key-row load at most, and the grid size below which blocks take fewer query tiles.
+constexpr int kMaxGroupHeads = 16;
+constexpr int kPassesPerKeyLoad = 128;
 constexpr int kMinBlocks = 2048;
-static_assert(kPassesPerKeyLoad <= kMaxHeads, "the passes' weights fit the weight array");
 
 template <bool FP8>
 struct FragT;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   // rows read by one lane group at the same chunk hit 16 different 16-byte bank groups
   // (rows are not padded: the global->LDS loads fill 1 KB contiguously).
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kStages * kHeadBytes];
-  __shared__ float w_lds[kBQ * kMaxHeads];
+  __shared__ float w_lds[kBQ * (MULTI ? kPassesPerKeyLoad : kMaxHeads)];
   auto swz = [](int r) {
     if constexpr (kCpr >= 16) return r & 15;
     else return (r / (16 / kCpr)) & (kCpr - 1);
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   // Head weights of the block's queries, pass-major ([tile][head][query]) so that the 16
   // lanes of a group read 16 consecutive words; consecutive threads write consecutive words
   // (walking the rows of one head first avoids 32-way bank conflicts on the transposing
-  // stores).  The host keeps n_qt * h_i <= kMaxHeads.
+  // stores).  The host keeps n_qt * h_i <= kPassesPerKeyLoad (MULTI) or h_i <= kMaxHeads.
   for (int i = tid; i < n_pass * kBQ; i += kIdxThreads) {
     const int jj = i / kBQ;
     const int row = i - jj * kBQ;
@@ -497,7 +497,8 @@ hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
 // output a block walks several consecutive 32-row query tiles (MULTI) with its key rows
 // resident and the query staging running on across tiles: up to kPassesPerKeyLoad (tile,
 // head) passes per key load, fewer tiles while the grid would hold fewer than kMinBlocks
-// blocks (measured 5-6% faster than 64-row single tiles at 8 heads).  Otherwise a block owns
+// blocks.  Measured at 8 heads against 64-row single tiles: 5-6% faster with 32 passes per
+// load, 12% with 64, 15% with 128; at 32 heads 6-8% slower (so up to 16 heads only).  Otherwise a block owns
 // one tile of 32 rows, or of 64 rows when few heads (at most 8) leave each block little MFMA
 // work per key-row load: the larger tile doubles the queries each key row serves (5% faster
 // at 8 heads, 3% slower at 32).  The 64-row tile and MULTI are kept to d_i <= 128, whose
@@ -518,7 +519,7 @@ hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
   const int64_t tiles32 = (nq + 31) / 32;
   if constexpr (D <= 128) {
     const bool single = opt.gate_rows || opt.cand || opt.pool_shift != 0;
-    int group_tiles = (single || h_i >= kPassesPerKeyLoad) ? 1 : kPassesPerKeyLoad / h_i;
+    int group_tiles = (single || h_i > kMaxGroupHeads) ? 1 : kPassesPerKeyLoad / h_i;
     while (group_tiles > 1 &&
            ((tiles32 + group_tiles - 1) / group_tiles) * n_pool_tiles < kMinBlocks)
       group_tiles /= 2;
