@@ -104,8 +104,9 @@ def test_indexer_fp8_scaled_and_general_tiles(gpu, d_i):
     _check_scores(scores, ref, rows, p)
 
 
-@pytest.mark.parametrize("h_i,d_i,dtype", [(4, 128, "bf16"), (8, 128, "bf16"),
-                                          (16, 128, "bf16"), (8, 64, "bf16"), (8, 128, "fp8")])
+@pytest.mark.parametrize("h_i,d_i,dtype", [(1, 128, "bf16"), (3, 64, "bf16"), (4, 128, "bf16"),
+                                          (8, 128, "bf16"), (12, 128, "bf16"), (16, 128, "bf16"),
+                                          (8, 64, "bf16"), (8, 128, "fp8"), (5, 32, "bf16")])
 def test_indexer_large_launch_few_heads(gpu, h_i, d_i, dtype):
     """Few heads over 131k pools in one launch of 1000 rows (thousands of blocks, both query
     tile sizes): every visible score bit-identical to 32-row calls, nothing written past a
@@ -132,9 +133,10 @@ def test_indexer_large_launch_few_heads(gpu, h_i, d_i, dtype):
     one = torch.full((nq, ld), float("nan"), device=gpu)
     B.index_scores(q, k, w, one, q_start=q_start)
     split = torch.full((nq, ld), float("nan"), device=gpu)
-    h0 = h_i // 2
+    h0 = max(1, h_i // 2)
     B.index_scores(q[:, :h0], k, w[:, :h0], split, q_start=q_start)
-    B.index_scores(q[:, h0:], k, w[:, h0:], split, q_start=q_start, accumulate=True)
+    if h0 < h_i:
+        B.index_scores(q[:, h0:], k, w[:, h0:], split, q_start=q_start, accumulate=True)
     ref = torch.full((nq, ld), float("nan"), device=gpu)
     for r0 in range(0, nq, 32):
         r1 = min(nq, r0 + 32)
