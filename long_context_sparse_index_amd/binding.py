@@ -109,6 +109,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace the caller did not pass: allocated from torch's caching allocator on the
+    current stream.  When the kernels go to another stream, the block is marked as used by
+    that stream, so that the allocator does not hand it out again before they finish."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
@@ -159,7 +169,7 @@ def topk(scores, idx, *, q_start: int, n_pools: int, ws=None, stream=None):
     assert scores.shape[0] == nq and idx.dtype == torch.int32 and idx.is_contiguous()
     need = topk_workspace_bytes(nq, n_pools, k)
     if need and ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        ws = _workspace(need, scores.device, stream)
     lib = load_library()
     _check(lib.dsa_topk(_ptr(scores), scores.stride(0), q_start, nq, n_pools, k, _ptr(idx),
                         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -183,8 +193,7 @@ def index_topk(q_idx, k_idx, w, idx, *, q_start: int = 0, n_pools: int | None = 
     assert w.dtype == torch.float32
     w_stride = 0 if w.dim() == 1 else w.stride(0)
     if ws is None:
-        ws = torch.empty(max(index_topk_workspace_bytes(nq, n_pools, k), 1), dtype=torch.uint8,
-                         device=q_idx.device)
+        ws = _workspace(index_topk_workspace_bytes(nq, n_pools, k), q_idx.device, stream)
     lib = load_library()
     _check(lib.dsa_index_topk(_ptr(q_idx), _row_stride(q_idx), _ptr(k_idx), k_idx.stride(0),
                               _ptr(w), w_stride, q_start, nq, n_pools, h_i, d_i,
@@ -221,7 +230,7 @@ def sparse_attn_bwd(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
         assert t.is_contiguous()
     need = sparse_attn_bwd_workspace_bytes(nq, h)
     if need and ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = _workspace(need, q.device, stream)
     lib = load_library()
     _check(lib.dsa_sparse_attn_bwd(_ptr(q), _ptr(kv), kv.stride(0), _ptr(v),
                                    0 if v is None else v.stride(0), _ptr(idx), idx.shape[1],
@@ -251,7 +260,7 @@ def sparse_attn_bwd_deterministic(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: fl
     if ws is None:
         need = sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk, d_v,
                                                              dv is not None)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws = _workspace(need, q.device, stream)
     lib = load_library()
     _check(lib.dsa_sparse_attn_bwd_deterministic(
         _ptr(q), _ptr(kv), kv.stride(0), _ptr(v), 0 if v is None else v.stride(0), _ptr(idx),
@@ -275,7 +284,7 @@ def forward_chunked(q_idx, k_idx, w, q, kv, o, lse, *, k: int, chunk: int, scale
     w_stride = 0 if w.dim() == 1 else w.stride(0)
     need = forward_chunked_workspace_bytes(n_pools, chunk, k)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = _workspace(need, q.device, stream)
     lib = load_library()
     _check(lib.dsa_forward_chunked(
         _ptr(q_idx), _row_stride(q_idx), _ptr(k_idx), k_idx.stride(0), _ptr(w), w_stride, h_i,

@@ -26,10 +26,6 @@
 #include <type_traits>
 
 #include "attn_common.hpp"
-
-#ifndef DSA_PV_PHASE1
-#define DSA_PV_PHASE1 9
-#endif
 #include "launch.hpp"
 
 namespace dsa {
@@ -238,8 +234,10 @@ void attn_fwd_pair_kernel(
   static_assert(DQK % 64 == 0 && DV % 32 == 0, "tile shapes");
   static_assert(pair_fits<DQK, DV, SEPARATE_V>(), "LDS budget");
   // P.V blocks of the current tile done in phase 1 of the loop body (next to the next tile's
-  // logits); the rest go to phase 2, where they cover the softmax.
-  constexpr int kN1 = DSA_PV_PHASE1 < kKS / 2 ? DSA_PV_PHASE1 : kKS / 2;
+  // logits); the rest go to phase 2, where they cover the softmax.  With 576/512 rows that
+  // is 9 of the 16 blocks in phase 1 and 7 beside the softmax.
+  constexpr int kPvPhase1 = 9;
+  constexpr int kN1 = kPvPhase1 < kKS / 2 ? kPvPhase1 : kKS / 2;
 
   __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pxchg[kPairXchgBytes];

@@ -413,6 +413,54 @@ def test_chunked_matches_separate_calls_and_is_chunk_invariant(gpu):
     assert_close(outs[0][0].numpy(), ro, "O")
 
 
+def _check_selection_order_all_rows(gpu, wl, q_i, k_i, w, idx, sub=1024):
+    """On every row, against that row's indexer scores (dsa_index_scores of its chunk, which
+    the sampled rows pin to the oracle bit for bit): the valid slots are in the order of a
+    full sort (score non-increasing, lower pool first on equal scores), and no visible pool
+    left out beats the last selected one (an equal score only with a higher pool index)."""
+    n, p, k = wl.n_tokens, wl.n_pools, wl.topk
+    ld = ((p + 3) // 4) * 4
+    scores = torch.empty((wl.chunk, ld), dtype=torch.float32, device=gpu)
+    cols = torch.arange(ld, device=gpu)
+    ninf = float("-inf")
+    for t0 in range(0, n, wl.chunk):
+        nq = min(wl.chunk, n - t0)
+        B.index_scores(q_i[t0:t0 + nq], k_i, w, scores[:nq], q_start=t0)
+        for r0 in range(0, nq, sub):
+            m = min(sub, nq - r0)
+            sc = scores[r0:r0 + m]
+            blk = idx[t0 + r0:t0 + r0 + m]
+            t = torch.arange(t0 + r0, t0 + r0 + m, device=gpu, dtype=torch.int64)
+            vis = torch.clamp((t + 1) // 4, max=p)
+            valid = blk >= 0
+            pos = blk.clamp(min=0).long()
+            g = torch.where(valid, torch.gather(sc, 1, pos),
+                            torch.full((m, k), ninf, device=gpu))
+            both = valid[:, 1:]
+            assert not bool(((g[:, 1:] > g[:, :-1]) & both).any()), "t0=%d: order" % t0
+            tie = (g[:, 1:] == g[:, :-1]) & both
+            assert not bool((tie & (blk[:, 1:] <= blk[:, :-1])).any()), "t0=%d: tie order" % t0
+            # the best visible pool that was not selected
+            picked = torch.zeros((m, ld + 1), dtype=torch.bool, device=gpu)
+            picked.scatter_(1, torch.where(valid, pos, torch.full_like(pos, ld)),
+                            torch.ones_like(valid))
+            left = (cols[None, :] < vis[:, None]) & ~picked[:, :ld]
+            rest = torch.where(left, sc, torch.full_like(sc, ninf))
+            del picked, left
+            c = valid.sum(1)
+            has_rest = c < vis
+            if not bool(has_rest.any()):
+                continue
+            last = torch.gather(g, 1, (c - 1).clamp(min=0)[:, None])[:, 0]
+            last_pool = torch.gather(blk, 1, (c - 1).clamp(min=0)[:, None])[:, 0]
+            best = rest.max(1).values
+            assert not bool((has_rest & (best > last)).any()), "t0=%d: a better pool left out" % t0
+            eq = (rest == last[:, None]) & has_rest[:, None]
+            first_eq = torch.where(eq, cols[None, :], torch.full_like(cols[None, :], ld)).min(1).values
+            assert not bool((first_eq <= last_pool.long()).any()), "t0=%d: tie left out" % t0
+    del scores
+
+
 def _full_size_forward(gpu, wl, check_rows):
     q_i, k_i, w = I.index_inputs(wl, gpu)
     q, kv, _ = I.attn_inputs(wl, gpu)
@@ -440,6 +488,8 @@ def _full_size_forward(gpu, wl, check_rows):
         dup = (srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] >= 0)
         assert not bool(dup.any())
     say("  structure ok on all %d rows" % n)
+    _check_selection_order_all_rows(gpu, wl, q_i, k_i, w, idx)
+    say("  selection order and threshold ok on all %d rows" % n)
     # sampled rows against the oracle
     rows = check_rows
     q_rows = host_bits(q_i[torch.from_numpy(rows).to(gpu)])

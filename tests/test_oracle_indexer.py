@@ -165,3 +165,47 @@ def test_scores_of_integer_inputs_are_exact_in_fp32():
     out = _scores(q, k, w, np.arange(8) + 16, 4)
     assert out[0, 0] == 2048.0 * w.sum()
     del rng
+
+
+def test_hand_worked_example_with_negative_weights():
+    # The head weight multiplies the ReLU'd dot product; it is not inside the ReLU.  Two heads
+    # of width 3, q_t = [[2, 0, -1], [1, 1, 1]], keys k0 = [1, 2, 3], k1 = [-1, 0, 2],
+    # w = [-1, 2].
+    #   pool 0: dots 2*1 + 0*2 - 1*3 = -1 and 1 + 2 + 3 = 6 -> -1*0 + 2*6 = 12
+    #   pool 1: dots -2 + 0 - 2 = -4 and -1 + 0 + 2 = 1 -> -1*0 + 2*1 = 2
+    # with w = [-2, -1] instead: pool 0 -> -2*0 - 1*6 = -6, pool 1 -> -2*0 - 1*1 = -1.
+    # Had the weight sat inside the ReLU (max(0, w*dot)) these would read 1*... = 13, 6, 2, 8.
+    q = np.array([[2, 0, -1], [1, 1, 1]], dtype=np.float32)
+    k = np.array([[1, 2, 3], [-1, 0, 2]], dtype=np.float32)
+    q = np.pad(q, ((0, 0), (0, 29)))  # d_i = 32 (zero columns change no dot product)
+    k = np.pad(k, ((0, 0), (0, 29)))
+    qb = _bf16_bits(q)[None]
+    kb = _bf16_bits(k)
+    pos = oracle.index_scores(qb, kb, np.array([-1.0, 2.0], np.float32), [7], 2)
+    neg = oracle.index_scores(qb, kb, np.array([-2.0, -1.0], np.float32), [7], 2)
+    assert pos[0].tolist() == [12.0, 2.0]
+    assert neg[0].tolist() == [-6.0, -1.0]
+
+
+def test_signed_per_row_weights_match_numpy_relu_sum():
+    # Per-token signed weights: I[t, s] = sum_j w[t, j] * max(0, q[t, j] . k[s]), written with
+    # numpy matmuls in float64 (every value is an exact integer multiple of 1/8, so the one
+    # fp32 rounding of the oracle is exact too).
+    rng = np.random.default_rng(7)
+    n, p, h, d = 72, 18, 5, 64
+    q = _rand_int(rng, (n, h, d), 4)
+    k = _rand_int(rng, (p, d), 4)
+    w = (rng.choice([-2.0, -1.0, -0.5, -0.125, 0.25, 1.0, 2.0], size=(n, h))).astype(np.float32)
+    rows = np.arange(n)
+    out = oracle.index_scores(_bf16_bits(q), _bf16_bits(k), w, rows, p)
+    dots = np.einsum("thd,sd->ths", q.astype(np.float64), k.astype(np.float64))
+    ref = np.einsum("th,ths->ts", w.astype(np.float64), np.maximum(dots, 0.0))
+    assert np.any(ref < 0) and np.any(ref > 0)
+    for t in range(n):
+        v = min(p, (t + 1) // 4)
+        assert np.array_equal(out[t, :v], ref[t, :v].astype(np.float32)), t
+        assert np.all(np.isneginf(out[t, v:]))
+    # a negated weight vector negates every score exactly (the ReLU does not see w)
+    neg = oracle.index_scores(_bf16_bits(q), _bf16_bits(k), -w, rows, p)
+    fin = np.isfinite(out)
+    assert np.array_equal(neg[fin], -out[fin] + 0.0)
