@@ -197,6 +197,32 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, con
 size_t dsa_sparse_attn_bwd_workspace_bytes(int64_t nq, int32_t h);
 
 /*
+ * dsa_sparse_attn_bwd_noalloc - dsa_sparse_attn_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight training or
+ * serving loops, harnesses that forbid allocation).  Same operands, results and arithmetic as
+ * dsa_sparse_attn_bwd (same kernels); the per-row deltas D = dO . O that dsa_sparse_attn_bwd
+ * keeps in its workspace go to a static device array of 2^22 floats (16 MiB) inside the
+ * library instead.  Each GPU the library runs on holds one such array until the process
+ * ends; the first call on a device looks up its address (hipGetSymbolAddress, no
+ * allocation).  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Every delta is written before it is read, so nothing needs clearing between
+ * calls.
+ *   Limit: nq * h <= 4194304 (e.g. 65536 query rows of 64 heads); a larger call returns
+ *   DSA_ERR_UNSUPPORTED before anything is launched (split the rows over several calls, or
+ *   use dsa_sparse_attn_bwd).
+ *   All calls on one GPU share its array: calls that overlap in time on one GPU (on
+ *   different streams, or from several threads) race on it and give wrong results.  Calls
+ *   ordered on one stream are safe.
+ *   Supported: as the forward.
+ */
+dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* kv, int64_t ld_kv,
+                                       const void* v, int64_t ld_v, const int32_t* idx,
+                                       int32_t k, const void* o, int32_t o_dtype,
+                                       const float* lse, const void* d_o, float* dq, float* dkv,
+                                       float* dv, int64_t nq, int64_t n_pools, int32_t h,
+                                       int32_t d_qk, int32_t d_v, float scale, void* stream);
+
+/*
  * dsa_sparse_attn_bwd_deterministic - dsa_sparse_attn_bwd with results that do not vary from
  * run to run (bit-identical dq, dkv, dv for the same inputs).  The pages train the layer but
  * print no backward; reproducible gradients are this library's option.  dK and dV are

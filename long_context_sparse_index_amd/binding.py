@@ -54,6 +54,8 @@ _SIGNATURES = {
     "dsa_sparse_attn_bwd": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
                              _I64, _I64, _I32, _I32, _I32, _F32, _P, _SZ, _P], ctypes.c_int),
     "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32], _SZ),
+    "dsa_sparse_attn_bwd_noalloc": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P,
+                                     _P, _I64, _I64, _I32, _I32, _I32, _F32, _P], ctypes.c_int),
     "dsa_sparse_attn_bwd_deterministic": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P,
                                            _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _F32, _P,
                                            _SZ, _P], ctypes.c_int),
@@ -239,6 +241,23 @@ def sparse_attn_bwd(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
                                    nq, n_pools, h, d_qk, d_v, float(scale), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(stream)))
+    return dq, dkv, dv
+
+
+def sparse_attn_bwd_noalloc(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
+                            v=None, dv=None, n_pools: int | None = None, stream=None):
+    """As sparse_attn_bwd, with the library's static scratch instead of a workspace (the call
+    allocates nothing; nq * h <= 2^22; overlapping calls on one GPU race)."""
+    nq, h, d_qk = q.shape
+    n_pools = kv.shape[0] if n_pools is None else n_pools
+    for t in (q, idx, o, lse, d_o, dq, dkv):
+        assert t.is_contiguous()
+    lib = load_library()
+    _check(lib.dsa_sparse_attn_bwd_noalloc(_ptr(q), _ptr(kv), kv.stride(0), _ptr(v),
+                                           0 if v is None else v.stride(0), _ptr(idx),
+                                           idx.shape[1], _ptr(o), _out_code(o), _ptr(lse),
+                                           _ptr(d_o), _ptr(dq), _ptr(dkv), _ptr(dv), nq, n_pools,
+                                           h, d_qk, d_v, float(scale), _stream(stream)))
     return dq, dkv, dv
 
 

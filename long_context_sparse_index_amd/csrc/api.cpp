@@ -321,6 +321,41 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, con
                     "dsa_sparse_attn_bwd launch");
 }
 
+dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* kv, int64_t ld_kv,
+                                       const void* v, int64_t ld_v, const int32_t* idx,
+                                       int32_t k, const void* o, int32_t o_dtype,
+                                       const float* lse, const void* d_o, float* dq, float* dkv,
+                                       float* dv, int64_t nq, int64_t n_pools, int32_t h,
+                                       int32_t d_qk, int32_t d_v, float scale, void* stream) {
+  if (dsa_status st = check_attn_args(q, kv, ld_kv, v, ld_v, idx, k, n_pools, h, d_qk, d_v,
+                                      scale))
+    return st;
+  if (dsa_status st = check_out_dtype(o_dtype)) return st;
+  DSA_REQUIRE(o && lse && d_o && dq && dkv, "attn_bwd_noalloc: null o, lse, d_o, dq or dkv");
+  DSA_REQUIRE(aligned(o, 16) && aligned(d_o, 16) && aligned(dq, 16) && aligned(dkv, 16) &&
+                  aligned(lse, 4),
+              "attn_bwd_noalloc: o, d_o, dq, dkv must be 16-byte aligned");
+  DSA_REQUIRE(!v || dv, "attn_bwd_noalloc: dv is required when a separate v is given");
+  DSA_REQUIRE(!dv || aligned(dv, 16), "attn_bwd_noalloc: dv must be 16-byte aligned");
+  DSA_REQUIRE(nq >= 0, "attn_bwd_noalloc: nq must be >= 0");
+  const int64_t cap = dsa::attn_bwd_scratch_floats();
+  if (nq > cap / h)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "attn_bwd_noalloc: nq * h = %lld * %d exceeds the static scratch of %lld "
+                "per-row deltas (use dsa_sparse_attn_bwd with a workspace)",
+                static_cast<long long>(nq), h, static_cast<long long>(cap));
+  if (nq == 0) return ok();
+  float* scratch = nullptr;
+  if (dsa_status st = hip_status(dsa::attn_bwd_scratch(&scratch),
+                                 "attn_bwd_noalloc: static scratch lookup"))
+    return st;
+  return hip_status(dsa::launch_sparse_attn_bwd(q, kv, ld_kv, v, ld_v, idx, k, o,
+                                                o_dtype == DSA_DTYPE_F32, lse, d_o, dq, dkv, dv,
+                                                nq, n_pools, h, d_qk, d_v, scale, scratch,
+                                                static_cast<hipStream_t>(stream)),
+                    "dsa_sparse_attn_bwd_noalloc launch");
+}
+
 size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
                                                          int64_t n_pools, int32_t d_qk,
                                                          int32_t d_v, int32_t separate_v) {

@@ -23,8 +23,18 @@
 // Probabilities and dS enter the MFMAs as bf16 hi + lo pairs (about 16 significant bits).
 // Summation order of the atomics varies from run to run.
 
+#include <mutex>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
+
+// Static scratch of the allocation-free backward entry point: the per-row deltas
+// D[t, h] = dO . O of one call, at most kBwdScratchFloats of them (16 MiB).  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): it uses the device address
+// that hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr long long kBwdScratchFloats = 1ll << 22;
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
 
 namespace dsa {
 namespace {
@@ -483,6 +493,29 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
 
 size_t attn_bwd_workspace_bytes(int64_t nq, int h) {
   return static_cast<size_t>(nq > 0 ? nq : 0) * static_cast<size_t>(h > 0 ? h : 0) * sizeof(float);
+}
+
+int64_t attn_bwd_scratch_floats() { return kBwdScratchFloats; }
+
+hipError_t attn_bwd_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = static_cast<float*>(addr[dev]);
+  return hipSuccess;
 }
 
 size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v) {

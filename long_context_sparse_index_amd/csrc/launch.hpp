@@ -67,6 +67,11 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* kv, int64_t ld_kv, 
                                   int d_v, float scale, hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(int64_t nq, int h);
+// The allocation-free backward keeps its per-row deltas in a static device array of this
+// many floats; attn_bwd_scratch gives that array's address on the current device (looked
+// up once per device, thread-safe).
+int64_t attn_bwd_scratch_floats();
+hipError_t attn_bwd_scratch(float** out);
 // Bytes of the fixed-point dK (and separate dV) accumulators of the deterministic backward.
 size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v);
 // fixed_ws (non-null): deterministic dK/dV through 64-bit fixed-point accumulators of

@@ -156,3 +156,21 @@ def test_fused_select_and_deterministic_backward_reject_bad_arguments(lib):
     need = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(4, 64, 100, 576, 512, 0)
     assert det(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None, 4,
                100, 64, 576, 512, 0.1, P(0x100000), need - 1, None) == 3
+
+
+def test_noalloc_backward_rejects_sizes_past_its_static_scratch(lib):
+    # nq * h above 2^22 per-row deltas is refused before any device call (this runs without
+    # a GPU); so are the argument errors of dsa_sparse_attn_bwd
+    nb = lib.dsa_sparse_attn_bwd_noalloc
+    F32 = 2
+    assert nb(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
+              65537, 100, 64, 576, 512, 0.1, None) == 2
+    assert b"static scratch" in lib.dsa_last_error()
+    assert nb(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
+              (1 << 22) + 1, 100, 1, 576, 512, 0.1, None) == 2
+    assert nb(FAKE, FAKE, 576, FAKE, 512, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
+              4, 100, 64, 576, 512, 0.1, None) == 1
+    assert nb(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, None, FAKE, None,
+              4, 100, 64, 576, 512, 0.1, None) == 1
+    assert nb(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
+              -1, 100, 64, 576, 512, 0.1, None) == 1
