@@ -9,7 +9,13 @@ launch duration; from it come per-phase rates and the roofline fraction of the d
 kernel (algorithmic bytes or flops per launch / measured duration / MI355X peak).  The CPU
 oracle is timed on a bounded sample of rows of the same workload (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+By default the line is the 128k forward (fwd_128k: value, config, roofline, cpu_baseline)
+and, after the 128k tensors are freed, the same measurement of one GPU's share of the 1M-token
+layer (tp_share_1m) as a nested object of the same line, so that both context lengths of the
+metric come from one run.  --workload NAME measures that workload alone; --second NAME (or
+"none") changes the nested one.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--second NAME]
 """
 
 from __future__ import annotations
@@ -35,6 +41,11 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 DEFAULT_WORKLOAD = "fwd_128k"
+SECOND_WORKLOAD = "tp_share_1m"
+# Timed steps of the nested 1M measurement are capped (one step is about 0.9 s) so that the
+# default run stays within a few minutes.
+SECOND_MAX_STEPS = 5
+SECOND_MAX_WARMUP = 2
 
 
 def parse():
@@ -42,7 +53,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help="measure this workload alone (default: %s, then %s nested)"
+                         % (DEFAULT_WORKLOAD, SECOND_WORKLOAD))
+    ap.add_argument("--second", default=None,
+                    help="workload measured after the first and nested in the same line "
+                         "(default %s with the default workload; 'none' to skip)"
+                         % SECOND_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,10 +129,11 @@ def main():
     import torch
 
     from long_context_sparse_index_amd import binding as B
-    from long_context_sparse_index_amd import inputs as I
     from long_context_sparse_index_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
+    first = args.workload or DEFAULT_WORKLOAD
+    second = args.second if args.second is not None else (
+        SECOND_WORKLOAD if args.workload is None else "none")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.load_library()
@@ -128,6 +146,26 @@ def main():
         torch.cuda.synchronize()
         print("bench: copy probe of %d bytes done" % nb, file=sys.stderr, flush=True)
         del src, dst
+    line = measure(W.WORKLOADS[first], args.steps, args.warmup, args, dev)
+    if second != "none":
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        sub = measure(W.WORKLOADS[second], min(args.steps, SECOND_MAX_STEPS),
+                      min(args.warmup, SECOND_MAX_WARMUP), args, dev)
+        line[second] = {key: sub[key] for key in (
+            "metric", "value", "unit", "steps", "warmup", "ms_per_step", "dtype", "config",
+            "roofline", "phases", "cpu_baseline")}
+    print(json.dumps(line), flush=True)
+
+
+def measure(wl, steps, warmup, args, dev):
+    """One workload: whole-forward steps timed, then the instrumented passes; returns the
+    fields of the JSON line."""
+    import torch
+
+    from long_context_sparse_index_amd import binding as B
+    from long_context_sparse_index_amd import inputs as I
+
     n, p, k, chunk = wl.n_tokens, wl.n_pools, wl.topk, wl.chunk
     has_attn = wl.heads > 0
     print("bench: workload %s (N=%d, P=%d, chunk %d)" % (wl.name, n, p, chunk),
@@ -191,25 +229,26 @@ def main():
     step = step_driver if has_attn else (lambda: step_select(None))
 
     # ---- timed region: whole forward steps
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    print("bench: %.3f ms/step (wall %.3f s for %d steps)" % (ms_per_step, wall, args.steps),
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    print("bench: %s %.3f ms/step (wall %.3f s for %d steps)" % (wl.name, ms_per_step, wall,
+                                                                 steps),
           file=sys.stderr, flush=True)
 
     # ---- instrumented pass: per-kernel launch durations on the launching stream
     events = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         step_phases(events)
     torch.cuda.synchronize()
     ph_ms = {"indexer": 0.0, "topk": 0.0, "attn_fwd": 0.0}
@@ -217,15 +256,15 @@ def main():
         ph_ms["indexer"] += e[0].elapsed_time(e[1])
         ph_ms["topk"] += e[1].elapsed_time(e[2])
         ph_ms["attn_fwd"] += e[2].elapsed_time(e[3])
-    per_step = {kname: v / args.steps for kname, v in ph_ms.items()}
+    per_step = {kname: v / steps for kname, v in ph_ms.items()}
     n_launch = len(chunks)
     # ---- the select (indexer + top-k) per chunk as the driver runs it
     sel_rec = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         step_select(sel_rec)
     torch.cuda.synchronize()
-    sel_fused = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if f) / args.steps
-    sel_two = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if not f) / args.steps
+    sel_fused = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if f) / steps
+    sel_two = sum(e[0].elapsed_time(e[1]) for f, e in sel_rec if not f) / steps
 
     # algorithmic work of one step
     pairs = visible_pairs(0, n, p)
@@ -294,8 +333,8 @@ def main():
 
     if has_attn and "attn_bwd" in wl.phases:
         idx_b = idx_for_bwd(wl, q_i, k_i, w, dev)
-        phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_b, args.steps, stream)
-        phases["attn_bwd_deterministic"] = time_backward(wl, q, kv, o, lse, idx_b, args.steps,
+        phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_b, steps, stream)
+        phases["attn_bwd_deterministic"] = time_backward(wl, q, kv, o, lse, idx_b, steps,
                                                          stream, deterministic=True)
 
     cpu = None
@@ -303,6 +342,10 @@ def main():
         cpu = cpu_baseline(wl, q_i, k_i, w, q if has_attn else None, kv if has_attn else None,
                            args.cpu_seconds)
 
+    # free this workload's device memory before the next one is generated
+    del q_i, k_i, w, scores, idx_chunk, sel_ws
+    if has_attn:
+        del q, kv, o, lse, ws
     value = n / (ms_per_step * 1e-3)
     line = {
         "metric": ("DSA forward tokens/s (indexer + top-k + sparse attention, chunked)"
@@ -310,8 +353,8 @@ def main():
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -328,7 +371,7 @@ def main():
         "phases": phases,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def idx_for_bwd(wl, q_i, k_i, w, dev):
@@ -403,8 +446,13 @@ def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):
     import oracle
     from long_context_sparse_index_amd import inputs as I
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-    threads = min(threads, 16)
+    # Every core this process may run on, unless the host assigns a smaller CPU share through
+    # OMP_NUM_THREADS (a GPU machine sets it to its per-GPU share): the thread count used is
+    # reported as `cores`, next to the host's core count.
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (
+        os.cpu_count() or 1)
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(share, usable) if share > 0 else usable
     rng = np.random.default_rng(1234)
     k_bits = I.index_bits(k_i)
     kv_bits = I.bits_u16(kv) if kv is not None else None
@@ -434,8 +482,11 @@ def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):
     n1 = max(1, min(wl.n_tokens, int(0.1 * budget_s * (nrows / max(dt, 1e-3)) / all_threads)))
     dt1 = run(n1)
     return {"value": nrows / dt, "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "host_cores": os.cpu_count(), "usable_cores": usable,
+            "threads_from": "OMP_NUM_THREADS" if share > 0 else "affinity",
             "sample": "%d uniformly sampled query rows of %s (seed 1234), all phases of the "
-                      "forward, %.1f s" % (nrows, wl.name, dt),
+                      "forward, %.1f s; tokens/s = rows / s (a uniform sample has the "
+                      "workload's mean cost per row)" % (nrows, wl.name, dt),
             "one_core": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
                          "sample": "%d sampled rows, %.1f s" % (n1, dt1)}}
 
