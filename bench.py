@@ -393,7 +393,8 @@ def idx_for_bwd(wl, q_i, k_i, w, dev):
 
 def time_backward(wl, q, kv, o, lse, idx, steps, stream, deterministic=False):
     """Times dsa_sparse_attn_bwd over the whole sequence (dQ, and dK / dV by fp32 atomics;
-    or dsa_sparse_attn_bwd_deterministic, fixed-point dK / dV) on the forward's outputs;
+    or dsa_sparse_attn_bwd_deterministic, staged dK / dV rows summed per pool in a fixed
+    order) on the forward's outputs;
     flops count the recomputed logits, dP, dV, dQ and dK."""
     import torch
 
@@ -407,7 +408,8 @@ def time_backward(wl, q, kv, o, lse, idx, steps, stream, deterministic=False):
     dkv = torch.zeros((p, wl.d_qk), dtype=torch.float32, device=q.device)
     if deterministic:
         ws = torch.empty(B.sparse_attn_bwd_deterministic_workspace_bytes(
-            n, wl.heads, p, wl.d_qk, wl.d_v, False), dtype=torch.uint8, device=q.device)
+            n, wl.heads, p, wl.topk, wl.d_qk, wl.d_v, False), dtype=torch.uint8,
+            device=q.device)
     else:
         ws = torch.empty(B.sparse_attn_bwd_workspace_bytes(n, wl.heads), dtype=torch.uint8,
                          device=q.device)
@@ -434,8 +436,9 @@ def time_backward(wl, q, kv, o, lse, idx, steps, stream, deterministic=False):
             "frac_of_mfma_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "tokens_per_s": n / (ms * 1e-3),
             "note": "%s over all rows (dQ, dKV with dV folded in), timed with the zeroing of "
-                    "dKV, %d launches" % ("dsa_sparse_attn_bwd_deterministic" if deterministic
-                                          else "dsa_sparse_attn_bwd", steps)}
+                    "dKV, %d launches" % ("dsa_sparse_attn_bwd_deterministic (no atomics)"
+                                          if deterministic else
+                                          "dsa_sparse_attn_bwd (fp32 atomics)", steps)}
 
 
 def cpu_baseline(wl, q_i, k_i, w, q, kv, budget_s):

@@ -224,18 +224,23 @@ dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* kv, int64_t ld
 
 /*
  * dsa_sparse_attn_bwd_deterministic - dsa_sparse_attn_bwd with results that do not vary from
- * run to run (bit-identical dq, dkv, dv for the same inputs).  The pages train the layer but
- * print no backward; reproducible gradients are this library's option.  dK and dV are
- * accumulated as signed 64-bit fixed-point numbers with 32 fractional bits (each
- * contribution rounded to a multiple of 2^-32, added with integer atomics, whose sum does
- * not depend on the order), then added into dkv (and dv) in fp32, one rounding per element.
+ * run to run (bit-identical dq, dkv, dv for the same inputs), without atomics.  The pages
+ * train the layer but print no backward; reproducible gradients are this library's option.
+ * dq is computed as in dsa_sparse_attn_bwd (it never used atomics).  For dK and dV the query
+ * rows go in chunks of up to 4096: each (row, slot) pair's head-summed dK row (with dV added
+ * into its first d_v columns when dv is NULL, or a separate dV row) is written to a staging
+ * buffer; the chunk's selection is sorted by pool with a stable radix sort, so that the pairs
+ * of every pool keep their row-major (row, slot) order; then each pool's staged rows are
+ * added in that order, in fp32, and the sum is added to the pool's row of dkv (and dv).
+ * Chunks are processed in row order.  Every sum therefore has a fixed order.
  *   Arguments as dsa_sparse_attn_bwd (dkv and dv are still accumulated: the caller zeroes
- *   them or keeps a running sum).
- *   ws: at least dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk, d_v,
- *   separate_v = (dv != NULL)) bytes, 256-byte aligned: the per-row deltas plus 8 bytes per
- *   dkv (and dv) element.
- *   Range: every partial sum of one element must stay below 2^31 in magnitude (a larger one
- *   wraps around); contributions below 2^-33 in magnitude are dropped.
+ *   them or keeps a running sum).  Any idx is accepted as for the forward (-1 or out-of-range
+ *   slots are skipped, a pool repeated in a row contributes once per slot).
+ *   ws: at least dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, k, d_qk,
+ *   d_v, separate_dv = (dv != NULL)) bytes, 256-byte aligned: the per-row deltas, the
+ *   staging rows of one chunk (min(nq, 4096) * k * (d_qk [+ d_v]) fp32, 19.3 GB for 4096 rows
+ *   of k = 2048 with 576-wide rows) and the sort buffers (about 20 bytes per pair plus 4 per
+ *   pool).
  *   Supported: as the forward.
  */
 dsa_status dsa_sparse_attn_bwd_deterministic(
@@ -244,8 +249,9 @@ dsa_status dsa_sparse_attn_bwd_deterministic(
     const void* d_o, float* dq, float* dkv, float* dv, int64_t nq, int64_t n_pools, int32_t h,
     int32_t d_qk, int32_t d_v, float scale, void* ws, size_t ws_bytes, void* stream);
 size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
-                                                         int64_t n_pools, int32_t d_qk,
-                                                         int32_t d_v, int32_t separate_v);
+                                                         int64_t n_pools, int32_t k,
+                                                         int32_t d_qk, int32_t d_v,
+                                                         int32_t separate_dv);
 
 /*
  * dsa_forward_chunked - the whole DSA forward over n_tokens queries, one query chunk at a

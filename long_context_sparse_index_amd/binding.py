@@ -59,8 +59,8 @@ _SIGNATURES = {
     "dsa_sparse_attn_bwd_deterministic": ([_P, _P, _I64, _P, _I64, _P, _I32, _P, _I32, _P, _P,
                                            _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _F32, _P,
                                            _SZ, _P], ctypes.c_int),
-    "dsa_sparse_attn_bwd_deterministic_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32, _I32],
-                                                          _SZ),
+    "dsa_sparse_attn_bwd_deterministic_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32, _I32,
+                                                           _I32], _SZ),
     "dsa_forward_chunked": ([_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P,
                              _I64, _I32, _I32, _I32, _F32, _I32, _I64, _I64, _I64, _P, _I32, _P,
                              _P, _P, _SZ, _P], ctypes.c_int),
@@ -261,24 +261,24 @@ def sparse_attn_bwd_noalloc(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d
     return dq, dkv, dv
 
 
-def sparse_attn_bwd_deterministic_workspace_bytes(nq: int, h: int, n_pools: int, d_qk: int,
-                                                  d_v: int, separate_v: bool) -> int:
+def sparse_attn_bwd_deterministic_workspace_bytes(nq: int, h: int, n_pools: int, k: int,
+                                                  d_qk: int, d_v: int, separate_dv: bool) -> int:
     return int(load_library().dsa_sparse_attn_bwd_deterministic_workspace_bytes(
-        nq, h, n_pools, d_qk, d_v, int(separate_v)))
+        nq, h, n_pools, k, d_qk, d_v, int(separate_dv)))
 
 
 def sparse_attn_bwd_deterministic(q, kv, idx, o, lse, d_o, dq, dkv, *, scale: float, d_v: int,
                                   v=None, dv=None, n_pools: int | None = None, ws=None,
                                   stream=None):
-    """As sparse_attn_bwd, with run-to-run identical dq, dkv and dv (fixed-point dK/dV
-    accumulation)."""
+    """As sparse_attn_bwd, with run-to-run identical dq, dkv and dv (no atomics: staged dK/dV
+    rows summed per pool in a fixed order)."""
     nq, h, d_qk = q.shape
     n_pools = kv.shape[0] if n_pools is None else n_pools
     for t in (q, idx, o, lse, d_o, dq, dkv):
         assert t.is_contiguous()
     if ws is None:
-        need = sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk, d_v,
-                                                             dv is not None)
+        need = sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, idx.shape[1], d_qk,
+                                                             d_v, dv is not None)
         ws = _workspace(need, q.device, stream)
     lib = load_library()
     _check(lib.dsa_sparse_attn_bwd_deterministic(

@@ -232,7 +232,7 @@ const char* dsa_status_string(dsa_status status) {
 
 const char* dsa_last_error(void) { return g_last_error; }
 
-int dsa_abi_version(void) { return 1; }
+int dsa_abi_version(void) { return 2; }
 
 dsa_status dsa_index_scores(const void* q_idx, int64_t q_row_stride, const void* k_idx,
                             int64_t k_row_stride, const float* w, int64_t w_row_stride,
@@ -357,11 +357,12 @@ dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* kv, int64_t ld
 }
 
 size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
-                                                         int64_t n_pools, int32_t d_qk,
-                                                         int32_t d_v, int32_t separate_v) {
-  if (d_qk <= 0 || d_v <= 0) return 0;
+                                                         int64_t n_pools, int32_t k,
+                                                         int32_t d_qk, int32_t d_v,
+                                                         int32_t separate_dv) {
+  if (nq <= 0 || h <= 0 || k <= 0 || d_qk <= 0 || d_v <= 0) return 0;
   return align256(dsa::attn_bwd_workspace_bytes(nq, h)) +
-         dsa::attn_bwd_fixed_bytes(n_pools, d_qk, d_v, separate_v != 0);
+         dsa::attn_bwd_det_bytes(nq, n_pools, k, d_qk, d_v, separate_dv != 0);
 }
 
 dsa_status dsa_sparse_attn_bwd_deterministic(
@@ -380,18 +381,19 @@ dsa_status dsa_sparse_attn_bwd_deterministic(
   DSA_REQUIRE(!v || dv, "attn_bwd_det: dv is required when a separate v is given");
   DSA_REQUIRE(!dv || aligned(dv, 16), "attn_bwd_det: dv must be 16-byte aligned");
   DSA_REQUIRE(nq >= 0, "attn_bwd_det: nq must be >= 0");
-  const size_t need = dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, d_qk,
+  if (nq == 0) return ok();
+  const size_t need = dsa_sparse_attn_bwd_deterministic_workspace_bytes(nq, h, n_pools, k, d_qk,
                                                                         d_v, dv != nullptr);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(DSA_ERR_WORKSPACE,
                 "attn_bwd_det: 256-byte aligned workspace of %zu bytes needed, %zu given", need,
                 ws ? ws_bytes : size_t{0});
   char* base = static_cast<char*>(ws);
-  void* fixed = base + align256(dsa::attn_bwd_workspace_bytes(nq, h));
+  void* det = base + align256(dsa::attn_bwd_workspace_bytes(nq, h));
   return hip_status(dsa::launch_sparse_attn_bwd(q, kv, ld_kv, v, ld_v, idx, k, o,
                                                 o_dtype == DSA_DTYPE_F32, lse, d_o, dq, dkv,
                                                 dv, nq, n_pools, h, d_qk, d_v, scale, ws,
-                                                static_cast<hipStream_t>(stream), fixed),
+                                                static_cast<hipStream_t>(stream), det),
                     "dsa_sparse_attn_bwd_deterministic launch");
 }
 

@@ -22,6 +22,12 @@
 //      dV buffer, the two contributions are added before the single atomic.
 // Probabilities and dS enter the MFMAs as bf16 hi + lo pairs (about 16 significant bits).
 // Summation order of the atomics varies from run to run.
+//
+// Deterministic variant: no atomics.  Query rows go in chunks; for each chunk the dkv kernel
+// writes every (row, slot) pair's head-summed dK (and dV) row to a staging buffer, then
+// bwd_reduce.hip sorts the chunk's selection by pool (stable, so pairs keep their row-major
+// order) and one workgroup per pool adds that pool's staged rows in that order into dkv (and
+// dv).  Chunks are reduced one after another, so every sum has a fixed order.
 
 #include <mutex>
 
@@ -215,7 +221,7 @@ struct DkvLds {
   static constexpr int kStageQ = kHeadsPad * (DQK + 8) * 2;
   static constexpr int kStageO = kHeadsPad * (DV + 8) * 2;
   static constexpr int kStage = kStageQ > kStageO ? kStageQ : kStageO;
-  static constexpr int kOther = 4 * kKeysPerTile * kPsRow * 2 + kMaxTopK * 4 + 64;
+  static constexpr int kOther = 4 * kKeysPerTile * kPsRow * 2 + kMaxTopK * 6 + 64;
   static constexpr int kTileBytes = TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes;
   // Tile stages share the staging region; deepest pipeline that fits beside the rest.
   static constexpr int kDepth = 3 * kTileBytes + kOther <= 160 * 1024 - 256   ? 3
@@ -236,29 +242,16 @@ __device__ __forceinline__ bf16x8 heads_operand(const uint16_t* x, int ld, int k
   return join_tr(lo, hi);
 }
 
-// Deterministic accumulation: each contribution becomes a signed 64-bit fixed-point value
-// with 32 fractional bits (value * 2^32, rounded to nearest), added with integer atomics.
-// Integer addition is associative, so the sums do not depend on the order in which tokens
-// arrive; a second pass converts them to fp32 once.  Valid while every partial sum stays
-// below 2^31 in magnitude; values below 2^-33 are lost.
-constexpr float kFixedScale = 4294967296.0f;  // 2^32
-
-template <bool FIXED>
-__device__ __forceinline__ void grad_add(void* base, int64_t i, float val) {
-  if constexpr (FIXED) {
-    const long long fx = __float2ll_rn(val * kFixedScale);
-    atomicAdd(static_cast<unsigned long long*>(base) + i, static_cast<unsigned long long>(fx));
-  } else {
-    atomicAdd(static_cast<float*>(base) + i, val);
-  }
-}
-
-template <int DQK, int DV, bool SEPARATE_V, bool FIXED>
+// STAGE = false: dkv [n_pools, DQK] and dv [n_pools, DV] (or nullptr: dV folded into dkv)
+// receive fp32 atomic adds.  STAGE = true: dkv and dv are staging buffers with one row per
+// (query row, slot) of this launch, row index row * k + slot, written (not added) for every
+// valid slot; dv nullptr again means dV folded into the dkv row.
+template <int DQK, int DV, bool SEPARATE_V, bool STAGE>
 __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
-    const float* __restrict__ delta, void* __restrict__ dkv, void* __restrict__ dv,
+    const float* __restrict__ delta, float* __restrict__ dkv, float* __restrict__ dv,
     int64_t n_pools, int h, float scale_log2, float scale) {
   using Lds = DkvLds<DQK, DV, SEPARATE_V>;
   using Dma = typename Lds::Dma;
@@ -268,6 +261,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t shared[Lds::kShared];  // staging, then tiles
   __shared__ __attribute__((aligned(16))) uint16_t ps[4][kKeysPerTile * kPsRow];
   __shared__ int32_t sel[kMaxTopK];
+  __shared__ int16_t slot_of[kMaxTopK];
   __shared__ int wave_tmp[kAttnThreads / 64];
   uint16_t* stage = reinterpret_cast<uint16_t*>(shared);
 
@@ -282,7 +276,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   const bool wave_has_heads = wid * 16 < h;
   const int col_base = wid * kCols;
 
-  const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
+  const int n_valid =
+      compact_selection(idx + row * k, k, n_pools, sel, wave_tmp, STAGE ? slot_of : nullptr);
   if (n_valid == 0) return;  // uniform: no selected row receives anything from this token
 
   // Operands with heads along the contraction, for this wave's columns: Q, then dO.
@@ -368,11 +363,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
         for (int ks = 0; ks < 2; ++ks)
           a[arr][ks] = *reinterpret_cast<const bf16x8*>(
               &ps[arr][(mb * 16 + r16) * kPsRow + 32 * ks + 8 * g]);
-      int32_t dst[4];
+      int64_t dst[4];  // gradient row (pool), or staging row (row * k + slot); -1: none
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = slot0 + mb * 16 + 4 * g + i;
-        dst[i] = slot < n_valid ? sel[slot] : -1;
+        if (STAGE)
+          dst[i] = slot < n_valid ? row * k + slot_of[slot] : -1;
+        else
+          dst[i] = slot < n_valid ? sel[slot] : -1;
       }
 #pragma unroll
       for (int nb = 0; nb < kNBW; ++nb) {
@@ -395,12 +393,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (dst[i] < 0) continue;
-          const int64_t kat = static_cast<int64_t>(dst[i]) * DQK + col;
-          if (fold_v) {
-            grad_add<FIXED>(dkv, kat, ak[i] * scale + (col0 < DV ? av[i] : 0.0f));
+          const int64_t kat = dst[i] * DQK + col;
+          const float gk = fold_v ? ak[i] * scale + (col0 < DV ? av[i] : 0.0f) : ak[i] * scale;
+          if (STAGE) {
+            dkv[kat] = gk;
+            if (!fold_v && col0 < DV) dv[dst[i] * DV + col] = av[i];
           } else {
-            grad_add<FIXED>(dkv, kat, ak[i] * scale);
-            if (col0 < DV) grad_add<FIXED>(dv, static_cast<int64_t>(dst[i]) * DV + col, av[i]);
+            atomicAdd(dkv + kat, gk);
+            if (!fold_v && col0 < DV) atomicAdd(dv + dst[i] * DV + col, av[i]);
           }
         }
       }
@@ -408,27 +408,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   });
 }
 
-// Fixed-point accumulators: cleared by a fill kernel (a memset node is avoided so that the
-// launch sequence can be captured in a graph), then added into the caller's fp32 buffer.
-__global__ __launch_bounds__(256) void fixed_zero_kernel(unsigned long long* __restrict__ a,
-                                                         int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    a[i] = 0ull;
-}
+// Query rows per chunk of the deterministic backward: its staging holds one dK (and dV) row
+// per (row, slot) of a chunk, e.g. 4096 * 2048 * 576 floats (19.3 GB) for 576-wide rows.
+constexpr int64_t kDetChunkRows = 4096;
 
-__global__ __launch_bounds__(256) void fixed_to_f32_add_kernel(
-    const unsigned long long* __restrict__ a, float* __restrict__ out, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const double v = static_cast<double>(static_cast<long long>(a[i])) * (1.0 / 4294967296.0);
-    out[i] += static_cast<float>(v);
-  }
-}
+struct DetLayout {
+  size_t stage_k, stage_v, reduce, total;
+};
 
-unsigned fill_grid(int64_t n) {
-  const int64_t b = (n + 255) / 256;
-  return static_cast<unsigned>(b < 4096 ? (b > 0 ? b : 1) : 4096);
+size_t align256(size_t b) { return (b + 255) & ~size_t{255}; }
+
+DetLayout det_layout(int64_t rows, int k, int64_t n_pools, int d_qk, int d_v, bool separate_dv) {
+  DetLayout L{};
+  const size_t pairs = static_cast<size_t>(rows > 0 ? rows : 0) * static_cast<size_t>(k);
+  size_t off = 0;
+  L.stage_k = off;
+  off += align256(pairs * d_qk * sizeof(float));
+  L.stage_v = off;
+  if (separate_dv) off += align256(pairs * d_v * sizeof(float));
+  L.reduce = off;
+  off += pool_reduce_workspace_bytes(static_cast<int64_t>(pairs), n_pools);
+  L.total = off;
+  return L;
 }
 
 template <int DQK, int DV, bool SEP>
@@ -436,7 +437,7 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
                         int64_t ld_v, const int32_t* idx, int k, const void* o, int o_f32,
                         const float* lse, const void* d_o, float* dq, float* dkv, float* dv,
                         int64_t nq, int64_t n_pools, int h, float scale, float* delta,
-                        unsigned long long* fixed, hipStream_t stream) {
+                        char* det_ws, hipStream_t stream) {
   const int64_t rows = nq * h;
   const unsigned dgrid = static_cast<unsigned>((rows + 3) / 4);
   if (o_f32)
@@ -448,45 +449,42 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = scale * kLog2e;
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kvb = static_cast<const uint16_t*>(kv);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
+  const uint16_t* dob = static_cast<const uint16_t*>(d_o);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, SEP>), dim3(static_cast<unsigned>(nq)),
-                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
-                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta, dq, n_pools, h,
-                     sl2, scale);
+                     dim3(kAttnThreads), 0, stream, qb, kvb, ld_kv, vb, ld_v, idx, k, lse, dob,
+                     delta, dq, n_pools, h, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!fixed) {
+  if (!det_ws) {
     hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, false>),
-                       dim3(static_cast<unsigned>(nq)), dim3(kAttnThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), ld_kv,
-                       static_cast<const uint16_t*>(v), ld_v, idx, k, lse,
-                       static_cast<const uint16_t*>(d_o), delta, static_cast<void*>(dkv),
-                       static_cast<void*>(dv), n_pools, h, sl2, scale);
+                       dim3(static_cast<unsigned>(nq)), dim3(kAttnThreads), 0, stream, qb, kvb,
+                       ld_kv, vb, ld_v, idx, k, lse, dob, delta, dkv, dv, n_pools, h, sl2,
+                       scale);
     return hipGetLastError();
   }
-  // Deterministic: fixed-point accumulators [n_pools, DQK] (and [n_pools, DV] for a
-  // separate dv) in the workspace.
-  const int64_t nk = n_pools * DQK, nv = dv ? n_pools * DV : 0;
-  unsigned long long* fk = fixed;
-  unsigned long long* fv = dv ? fixed + nk : nullptr;
-  hipLaunchKernelGGL(fixed_zero_kernel, dim3(fill_grid(nk + nv)), dim3(256), 0, stream, fixed,
-                     nk + nv);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, true>), dim3(static_cast<unsigned>(nq)),
-                     dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(kv), ld_kv, static_cast<const uint16_t*>(v),
-                     ld_v, idx, k, lse, static_cast<const uint16_t*>(d_o), delta,
-                     static_cast<void*>(fk), static_cast<void*>(fv), n_pools, h, sl2, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fixed_to_f32_add_kernel, dim3(fill_grid(nk)), dim3(256), 0, stream, fk,
-                     dkv, nk);
-  e = hipGetLastError();
-  if (e != hipSuccess || !dv) return e;
-  hipLaunchKernelGGL(fixed_to_f32_add_kernel, dim3(fill_grid(nv)), dim3(256), 0, stream, fv, dv,
-                     nv);
-  return hipGetLastError();
+  // Deterministic: chunk by chunk, staged rows, then the ordered per-pool reduction.
+  const int64_t chunk = nq < kDetChunkRows ? nq : kDetChunkRows;
+  const DetLayout L = det_layout(chunk, k, n_pools, DQK, DV, dv != nullptr);
+  float* stage_k = reinterpret_cast<float*>(det_ws + L.stage_k);
+  float* stage_v = dv ? reinterpret_cast<float*>(det_ws + L.stage_v) : nullptr;
+  void* red = det_ws + L.reduce;
+  for (int64_t r0 = 0; r0 < nq; r0 += chunk) {
+    const int64_t m = nq - r0 < chunk ? nq - r0 : chunk;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, true>),
+                       dim3(static_cast<unsigned>(m)), dim3(kAttnThreads), 0, stream,
+                       qb + r0 * h * DQK, kvb, ld_kv, vb, ld_v, idx + r0 * k, k, lse + r0 * h,
+                       dob + r0 * h * DV, delta + r0 * h, stage_k, stage_v, n_pools, h, sl2,
+                       scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_pool_reduce(idx + r0 * k, m, k, n_pools, stage_k, DQK, dkv, stage_v, DV, dv, red,
+                           stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -518,10 +516,11 @@ hipError_t attn_bwd_scratch(float** out) {
   return hipSuccess;
 }
 
-size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v) {
-  const int64_t p = n_pools > 0 ? n_pools : 0;
-  return static_cast<size_t>(p) * static_cast<size_t>(d_qk + (separate_v ? d_v : 0)) *
-         sizeof(unsigned long long);
+size_t attn_bwd_det_bytes(int64_t nq, int64_t n_pools, int k, int d_qk, int d_v,
+                          bool separate_dv) {
+  if (nq <= 0 || k <= 0 || d_qk <= 0 || d_v <= 0) return 0;
+  const int64_t chunk = nq < kDetChunkRows ? nq : kDetChunkRows;
+  return det_layout(chunk, k, n_pools > 0 ? n_pools : 0, d_qk, d_v, separate_dv).total;
 }
 
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
@@ -529,18 +528,20 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, 
                                   int o_f32, const float* lse, const void* d_o, float* dq,
                                   float* dkv, float* dv, int64_t nq, int64_t n_pools, int h,
                                   int d_qk, int d_v, float scale, void* ws,
-                                  hipStream_t stream, void* fixed_ws) {
+                                  hipStream_t stream, void* det_ws) {
   if (nq <= 0) return hipSuccess;
   if (nq * h >= (int64_t{1} << 33)) return hipErrorInvalidConfiguration;
+  if (det_ws && (nq < kDetChunkRows ? nq : kDetChunkRows) * k >= (int64_t{1} << 31))
+    return hipErrorInvalidConfiguration;
   float* delta = static_cast<float*>(ws);
-  unsigned long long* fixed = static_cast<unsigned long long*>(fixed_ws);
+  char* det = static_cast<char*>(det_ws);
 #define DSA_BWD(DQ, DVV)                                                                      \
   return v ? launch_bwd_t<DQ, DVV, true>(q, kv, ld_kv, v, ld_v, idx, k, o, o_f32, lse, d_o,   \
-                                         dq, dkv, dv, nq, n_pools, h, scale, delta, fixed,    \
+                                         dq, dkv, dv, nq, n_pools, h, scale, delta, det,      \
                                          stream)                                              \
            : launch_bwd_t<DQ, DVV, false>(q, kv, ld_kv, nullptr, 0, idx, k, o, o_f32, lse,    \
                                           d_o, dq, dkv, dv, nq, n_pools, h, scale, delta,     \
-                                          fixed, stream)
+                                          det, stream)
   if (d_qk == 128 && d_v == 128) DSA_BWD(128, 128);
   if (d_qk == 576 && d_v == 512) DSA_BWD(576, 512);
   if (d_qk == 512 && d_v == 512) DSA_BWD(512, 512);

@@ -23,9 +23,11 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
 // slot, and any other value is skipped the same way so that no gather leaves the table)
 // into sel[], in slot order, and returns their count.  All threads of the block call it.
 // Thread i takes the m = ceil(k / threads) consecutive slots [i m, i m + m), all loaded in
-// one memory round trip; a block prefix sum over the per-thread counts places them.
+// one memory round trip; a block prefix sum over the per-thread counts places them.  When
+// slot_of is given, slot_of[j] receives the original slot of compacted entry j.
 __device__ inline int compact_selection(const int32_t* __restrict__ irow, int k,
-                                        int64_t n_pools, int32_t* sel, int* wave_tmp) {
+                                        int64_t n_pools, int32_t* sel, int* wave_tmp,
+                                        int16_t* slot_of = nullptr) {
   constexpr int kMaxPer = kMaxTopK / kAttnThreads;
   constexpr int kWaves = kAttnThreads / 64;
   const int lane = threadIdx.x & 63;
@@ -56,7 +58,10 @@ __device__ inline int compact_selection(const int32_t* __restrict__ irow, int k,
   }
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i)
-    if (v[i] >= 0 && v[i] < n_pools) sel[off++] = v[i];
+    if (v[i] >= 0 && v[i] < n_pools) {
+      if (slot_of) slot_of[off] = static_cast<int16_t>(s0 + i);
+      sel[off++] = v[i];
+    }
   __syncthreads();
   return total;
 }

@@ -72,15 +72,27 @@ size_t attn_bwd_workspace_bytes(int64_t nq, int h);
 // up once per device, thread-safe).
 int64_t attn_bwd_scratch_floats();
 hipError_t attn_bwd_scratch(float** out);
-// Bytes of the fixed-point dK (and separate dV) accumulators of the deterministic backward.
-size_t attn_bwd_fixed_bytes(int64_t n_pools, int d_qk, int d_v, bool separate_v);
-// fixed_ws (non-null): deterministic dK/dV through 64-bit fixed-point accumulators of
-// attn_bwd_fixed_bytes(...) bytes, 8-byte aligned; null: fp32 atomics.
+// Bytes of the deterministic backward's own workspace (staging rows of one query chunk and
+// the per-pool reduction's sort buffers), beside the per-row deltas.
+size_t attn_bwd_det_bytes(int64_t nq, int64_t n_pools, int k, int d_qk, int d_v,
+                          bool separate_dv);
+// det_ws (non-null, 256-byte aligned, attn_bwd_det_bytes(...) bytes): deterministic dK/dV
+// (staged rows reduced per pool in a fixed order); null: fp32 atomics.
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
                                   int64_t ld_v, const int32_t* idx, int k, const void* o,
                                   int o_f32, const float* lse, const void* d_o, float* dq, float* dkv,
                                   float* dv, int64_t nq, int64_t n_pools, int h, int d_qk,
                                   int d_v, float scale, void* ws, hipStream_t stream,
-                                  void* fixed_ws = nullptr);
+                                  void* det_ws = nullptr);
+
+// Deterministic per-pool sums of staged rows (bwd_reduce.hip).  idx [rows, k] is the
+// selection of the staged chunk; stage_k [rows * k, w_k] (and stage_v [rows * k, w_v], or
+// null) hold one row per (row, slot).  out_k[s] (and out_v[s]) += the rows of the pairs that
+// selected pool s, added in row-major (row, slot) order.  ws: pool_reduce_workspace_bytes.
+size_t pool_reduce_workspace_bytes(int64_t n_entries, int64_t n_pools);
+hipError_t launch_pool_reduce(const int32_t* idx, int64_t rows, int k, int64_t n_pools,
+                              const float* stage_k, int w_k, float* out_k,
+                              const float* stage_v, int w_v, float* out_v, void* ws,
+                              hipStream_t s);
 
 }  // namespace dsa

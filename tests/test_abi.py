@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(2) == b"DSA_ERR_UNSUPPORTED"
 
@@ -124,12 +124,26 @@ def test_fused_select_and_deterministic_workspaces(lib):
     # k above the fused select's limit: score chunk, index chunk and top-k workspace only
     assert (lib.dsa_forward_chunked_workspace_bytes(32768, 8192, 3000)
             < lib.dsa_index_topk_workspace_bytes(8192, 32768, 2048))
-    # deterministic backward: the per-row deltas plus 8 bytes per dK (and dV) element
+    # deterministic backward: the per-row deltas, one staged fp32 dK (and dV) row per
+    # (row, slot) of a chunk of at most 4096 rows, and the sort buffers (4 arrays of one int32
+    # per pair, digit histograms, pool bounds)
     base = lib.dsa_sparse_attn_bwd_workspace_bytes(100, 64)
-    det = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 576, 512, 0)
-    det_v = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 576, 512, 1)
-    assert det >= base + 5000 * 576 * 8
-    assert det_v - det == 5000 * 512 * 8
+    det = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 2048, 576, 512, 0)
+    det_v = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(100, 64, 5000, 2048, 576, 512,
+                                                                  1)
+    pairs = 100 * 2048
+    assert det >= base + pairs * 576 * 4 + 4 * pairs * 4 + 5001 * 4
+    assert det_v - det == pairs * 512 * 4
+    # chunks of 4096 rows: the staging does not grow past them
+    big = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(65536, 64, 16384, 2048, 576,
+                                                                512, 0)
+    mid = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(4096, 64, 16384, 2048, 576,
+                                                                512, 0)
+    assert big - mid == (lib.dsa_sparse_attn_bwd_workspace_bytes(65536, 64)
+                         - lib.dsa_sparse_attn_bwd_workspace_bytes(4096, 64))
+    assert mid >= 4096 * 2048 * 576 * 4
+    assert lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(0, 64, 100, 2048, 576, 512,
+                                                                 0) == 0
 
 
 def test_fused_select_and_deterministic_backward_reject_bad_arguments(lib):
@@ -153,7 +167,7 @@ def test_fused_select_and_deterministic_backward_reject_bad_arguments(lib):
                4, 100, 64, 576, 512, 0.1, FAKE, 1 << 30, None) == 1
     assert det(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None, 4,
                100, 64, 576, 256, 0.1, FAKE, 1 << 30, None) == 2
-    need = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(4, 64, 100, 576, 512, 0)
+    need = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(4, 64, 100, 2048, 576, 512, 0)
     assert det(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None, 4,
                100, 64, 576, 512, 0.1, P(0x100000), need - 1, None) == 3
 

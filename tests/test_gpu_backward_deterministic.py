@@ -1,7 +1,7 @@
 """GPU tests of the deterministic backward (dsa_sparse_attn_bwd_deterministic): gradients
-within the backward's tolerance of the CPU oracle, bit-identical across repeated calls (the
-fixed-point dK/dV sums do not depend on the order of the atomics), and within tolerance of
-the fp32-atomic backward."""
+within the backward's tolerance of the CPU oracle, bit-identical across repeated calls (no
+atomics: every pool's staged dK/dV rows are summed in row-major order after a stable sort by
+pool), and within tolerance of the fp32-atomic backward."""
 
 import numpy as np
 import pytest
@@ -138,3 +138,41 @@ def test_deterministic_backward_full_size_64k(gpu):
     sum_do = d_o.float()[has].sum(dim=(0, 1)).double()
     scale_do = d_o.float()[has].abs().sum(dim=(0, 1)).double()
     assert float(((a[2].double().sum(0) - sum_do).abs() / scale_do).max()) < 1e-4
+
+
+def test_deterministic_backward_two_chunks_repeats_and_junk(gpu):
+    """5000 query rows (two chunks of the staged reduction: 4096 + 904), selections with
+    repeated pools in a row, -1 anywhere and out-of-range values (skipped like -1): bit-identical
+    across calls, dQ bit-identical to the atomic backward, and dK / dV within tolerance of the
+    oracle (given the same selection with the out-of-range values as -1)."""
+    say("case: deterministic backward two chunks, repeated pools and junk slots")
+    nq, p, k, h, d = 5000, 700, 96, 8, 128
+    g = torch.Generator(device=gpu).manual_seed(11)
+    q = torch.randn((nq, h, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    kv = torch.randn((p, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    v = torch.randn((p, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    d_o = torch.randn((nq, h, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    idx = torch.randint(0, p, (nq, k), generator=g, device=gpu, dtype=torch.int32)
+    idx[:, 5] = idx[:, 2]  # a pool repeated in every row
+    junk = torch.rand((nq, k), generator=g, device=gpu)
+    idx[junk < 0.05] = -1
+    idx[(junk >= 0.05) & (junk < 0.08)] = p + 3  # out of range: skipped like -1
+    idx[(junk >= 0.08) & (junk < 0.09)] = -5
+    idx[4100:4110] = -1  # rows without a valid slot in the second chunk
+    idx = idx.contiguous()
+    scale = 1.0 / float(np.sqrt(d))
+    o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=scale, d_v=d, v=v)
+    a = _bwd(True, q, kv, idx, o, lse, d_o, scale, d, v=v)
+    b = _bwd(True, q, kv, idx, o, lse, d_o, scale, d, v=v)
+    assert all(_same_bits(x, y) for x, y in zip(a, b)), "not reproducible"
+    at = _bwd(False, q, kv, idx, o, lse, d_o, scale, d, v=v)
+    assert _same_bits(a[0], at[0])
+    assert_close(a[1].cpu().numpy(), at[1].cpu().numpy(), "dK vs fp32 atomics")
+    assert_close(a[2].cpu().numpy(), at[2].cpu().numpy(), "dV vs fp32 atomics")
+    clean = idx.cpu().numpy().copy()
+    clean[(clean < 0) | (clean >= p)] = -1
+    rq, rk, rv = oracle.sparse_attn_bwd(host_bits(q), host_bits(kv), clean, host_bits(d_o),
+                                        scale, v_bits=host_bits(v), d_v=d)
+    assert_close(a[0].cpu().numpy(), rq, "dQ")
+    assert_close(a[1].cpu().numpy(), rk, "dK")
+    assert_close(a[2].cpu().numpy(), rv, "dV")

@@ -51,7 +51,7 @@ def test_side_stream_forward_and_backward_without_workspace(gpu):
         B.sparse_attn_bwd_deterministic(q, kv, idx, o, lse, d_o, dq, dkv, scale=TINY.scale,
                                         d_v=TINY.d_v, stream=side)
         need_b = B.sparse_attn_bwd_deterministic_workspace_bytes(
-            TINY.n_tokens, TINY.heads, TINY.n_pools, TINY.d_qk, TINY.d_v, False)
+            TINY.n_tokens, TINY.heads, TINY.n_pools, TINY.topk, TINY.d_qk, TINY.d_v, False)
         junk += [torch.full((need_b,), 0x7F, dtype=torch.uint8, device=gpu) for _ in range(2)]
         torch.cuda.synchronize()
         assert torch.equal(idx, ref_idx)
