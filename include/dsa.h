@@ -160,9 +160,11 @@ size_t dsa_index_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k);
  *   are the latent row without its rotary columns, NoPE, full and half width),
  *   1 <= h <= 64, 1 <= k <= 4096 (any k, e.g. 2051).
  *   Slots holding a value outside [-1, n_pools) are skipped like -1 (never dereferenced).
- * Arithmetic: bf16 MFMA for q.K with fp32 accumulation, fp32 online softmax; each
- * probability enters the P.V MFMA as a pair of bf16 values (its rounding and the rounding
- * of the remainder), so P is carried to about 16 bits; fp32 accumulation of O.
+ * Arithmetic: bf16 MFMA for q.K with fp32 accumulation, fp32 softmax; on rows with fewer
+ * than 512 valid slots each probability enters the P.V MFMA as a pair of bf16 values (its
+ * rounding and the rounding of the remainder, about 16 significant bits), on longer rows as
+ * one bf16 value (8 bits; a relative error of at most 2^-8 per probability, about 1e-3 of
+ * the RMS of O on average); fp32 accumulation of O and of the row sums.
  */
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv, int64_t ld_kv, const void* v,
                                int64_t ld_v, const int32_t* idx, int32_t k, void* o,

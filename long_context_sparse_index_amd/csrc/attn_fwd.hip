@@ -35,6 +35,15 @@ namespace {
 // of the P.V product tolerates (probabilities up to 2^64, sums far below fp32 overflow).
 constexpr float kRefHeadroomLog2 = 64.0f;
 
+// Rows with fewer valid slots than this feed the P.V product each probability as a bf16
+// pair hi + lo (about 16 significant bits); rows with more feed one bf16 (8 bits, half the
+// P.V MFMAs).  The rounding of p to bf16 is a relative error of at most 2^-8 per key, random
+// in sign, so O of a row with c keys carries a relative error of about 1.6e-3 of its own
+// magnitude, which is about sqrt(e / c) for N(0, 1) logits: at c >= 512 that stays far
+// inside 2e-2 of the RMS of O over any set of rows (whose RMS is at least that of the
+// many-key rows); rows with few keys (|O| up to the size of one value row) need the pair.
+constexpr int kSplitBelow = 512;
+
 template <int DQK, int DV, bool SEPARATE_V, bool OUT_F32>
 __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
@@ -197,7 +206,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(
 //     half of the 16-byte operand into one shared LDS slot per lane and read back the
 //     whole operand after the tile barrier;
 //   * it accumulates O^T of the 32 heads over value-column half kh, so each transpose
-//     read of V feeds four MFMAs (two head groups x the hi/lo halves of P).
+//     read of V feeds four MFMAs (two head groups x the hi/lo halves of P), or two on rows
+//     with at least kSplitBelow valid slots, whose P is one bf16 value.
 // Per tile and block this halves the transpose reads and the key reads of the kernel
 // above, and no softmax work is done twice.  The pair shares one softmax reference per
 // head (the maximum of tile 0 over both key halves, exchanged once per pass) and adds its
@@ -238,6 +248,11 @@ void attn_fwd_pair_kernel(
   // is 9 of the 16 blocks in phase 1 and 7 beside the softmax.
   constexpr int kPvPhase1 = 9;
   constexpr int kN1 = kPvPhase1 < kKS / 2 ? kPvPhase1 : kKS / 2;
+  // With one bf16 per probability a block is two MFMAs: phase 1 takes one block per slot for
+  // its first kPvPhase1Single slots, phase 2 the rest beside the softmax (12 of 16 blocks
+  // with 576/512 rows: 2.79-2.88 ms per 8192-row 128k chunk on MI355X against 2.81-2.91
+  // with 9, 2.86-2.91 with 16 and 2.90-2.99 with 6).
+  constexpr int kPvPhase1Single = 12;
 
   __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pxchg[kPairXchgBytes];
@@ -357,7 +372,10 @@ void attn_fwd_pair_kernel(
   };
   // Probabilities p = 2^y of this wave's keys, summed into l_run, and written as bf16
   // hi + lo pairs into this wave's half of the exchange slots.
-  auto probabilities = [&](const f32x4 (&y)[2], int buf, float (&l_run)[2], float (&ymax)[2]) {
+  // (SPLIT: the bf16 pair hi + lo; otherwise hi only.)
+  auto probabilities = [&](const f32x4 (&y)[2], int buf, float (&l_run)[2], float (&ymax)[2],
+                           auto split) {
+    constexpr bool SPLIT = decltype(split)::value;
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) {
       ymax[hg] = __builtin_fmaxf(ymax[hg], max4(y[hg]));
@@ -366,20 +384,23 @@ void attn_fwd_pair_kernel(
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(y[hg][i]);
       l_run[hg] += (p[0] + p[1]) + (p[2] + p[3]);
       const bf16x4 hi = __builtin_convertvector(p, bf16x4);
-      const bf16x4 lo = __builtin_convertvector(p - __builtin_convertvector(hi, f32x4), bf16x4);
       *(lds_i16x4*)(pslot(buf, hg, 0) + 8 * kh) = __builtin_bit_cast(i16x4, hi);
-      *(lds_i16x4*)(pslot(buf, hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+      if constexpr (SPLIT) {
+        const bf16x4 lo =
+            __builtin_convertvector(p - __builtin_convertvector(hi, f32x4), bf16x4);
+        *(lds_i16x4*)(pslot(buf, hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+      }
     }
   };
-  auto read_probabilities = [&](int buf, bf16x8 (&phi)[2], bf16x8 (&plo)[2]) {
+  auto read_probabilities = [&](int buf, bf16x8 (&phi)[2], bf16x8 (&plo)[2], auto split) {
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) {
       phi[hg] = lds_load_bf16x8((lds_ptr)pslot(buf, hg, 0));
-      plo[hg] = lds_load_bf16x8((lds_ptr)pslot(buf, hg, 1));
+      if constexpr (decltype(split)::value) plo[hg] = lds_load_bf16x8((lds_ptr)pslot(buf, hg, 1));
     }
   };
   // O^T += V^T . P^T over the 32 keys of a tile, value half kh.
-  auto pv_tile = [&](int st, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2]) {
+  auto pv_tile = [&](int st, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2], auto split) {
     const lds_ptr vb[4] = {pinned(st, v_lane[0]), pinned(st, v_lane[1]), pinned(st, v_lane[2]),
                            pinned(st, v_lane[3])};
 #pragma unroll
@@ -388,9 +409,11 @@ void attn_fwd_pair_kernel(
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg)
         oacc[hg][nb] = mfma16x16x32_bf16(vt, phi[hg], oacc[hg][nb]);
+      if constexpr (decltype(split)::value) {
 #pragma unroll
-      for (int hg = 0; hg < 2; ++hg)
-        oacc[hg][nb] = mfma16x16x32_bf16(vt, plo[hg], oacc[hg][nb]);
+        for (int hg = 0; hg < 2; ++hg)
+          oacc[hg][nb] = mfma16x16x32_bf16(vt, plo[hg], oacc[hg][nb]);
+      }
     }
   };
 
@@ -413,8 +436,16 @@ void attn_fwd_pair_kernel(
     ah.v0 = join_tr(lds_read_tr16_at(v0), lds_read_tr16_at(v0 + kVHi));
   };
   auto fused_step = [&](int st_k, int st_v, int t1, const Ahead& ah, const bf16x8 (&phi)[2],
-                        const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2]) {
+                        const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2],
+                        auto split) {
+    constexpr bool SPLIT = decltype(split)::value;
     static_assert(kKS % 2 == 0 && kKS / 2 <= kNBH, "pipeline shape");
+    // P.V blocks in phase 1: SPLIT, half a block (two MFMAs) in each of the first 2 kN1
+    // slots; otherwise one whole block (two MFMAs) in each of the first kN1s slots.
+    constexpr int kN1s = kPvPhase1Single < kKS
+                             ? (kPvPhase1Single < kNBH ? kPvPhase1Single : kNBH)
+                             : (kKS < kNBH ? kKS : kNBH);
+    constexpr int kP1 = SPLIT ? kN1 : kN1s;  // blocks done in phase 1
     const lds_ptr kb[2] = {pinned(st_k, k_lane[0]), pinned(st_k, k_lane[1])};
     const lds_ptr vb[4] = {pinned(st_v, v_lane[0]), pinned(st_v, v_lane[1]),
                            pinned(st_v, v_lane[2]), pinned(st_v, v_lane[3])};
@@ -428,16 +459,27 @@ void attn_fwd_pair_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kKS; ++j) {
-      const int n = j / 2;
-      const bool pv = n < kN1;  // slots 0 .. 2 kN1 - 1 also carry half a P.V block
       if (j + 2 < kKS) ka[(j + 2) % 3] = lds_load_bf16x8(kb[j & 1] + ((j + 2) >> 1) * 1024);
-      if (pv && (j & 1) == 0 && n + 1 < kNBH) vf[(n + 1) & 1] = vt_block(vb, n + 1);
-      s[0][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[0][j], s[0][j & 1]);
-      s[1][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[1][j], s[1][j & 1]);
-      if (pv) {
-        const bf16x8(&pp)[2] = (j & 1) ? plo : phi;
-        oacc[0][n] = mfma16x16x32_bf16(vf[n & 1], pp[0], oacc[0][n]);
-        oacc[1][n] = mfma16x16x32_bf16(vf[n & 1], pp[1], oacc[1][n]);
+      if constexpr (SPLIT) {
+        const int n = j / 2;
+        const bool pv = n < kN1;  // slots 0 .. 2 kN1 - 1 also carry half a P.V block
+        if (pv && (j & 1) == 0 && n + 1 < kNBH) vf[(n + 1) & 1] = vt_block(vb, n + 1);
+        s[0][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[0][j], s[0][j & 1]);
+        s[1][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[1][j], s[1][j & 1]);
+        if (pv) {
+          const bf16x8(&pp)[2] = (j & 1) ? plo : phi;
+          oacc[0][n] = mfma16x16x32_bf16(vf[n & 1], pp[0], oacc[0][n]);
+          oacc[1][n] = mfma16x16x32_bf16(vf[n & 1], pp[1], oacc[1][n]);
+        }
+      } else {
+        const bool pv = j < kN1s;
+        if (pv && j + 1 < kNBH) vf[(j + 1) & 1] = vt_block(vb, j + 1);
+        s[0][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[0][j], s[0][j & 1]);
+        s[1][j & 1] = mfma16x16x32_bf16(ka[j % 3], qf[1][j], s[1][j & 1]);
+        if (pv) {
+          oacc[0][j] = mfma16x16x32_bf16(vf[j & 1], phi[0], oacc[0][j]);
+          oacc[1][j] = mfma16x16x32_bf16(vf[j & 1], phi[1], oacc[1][j]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -459,14 +501,16 @@ void attn_fwd_pair_kernel(
         l_run[hg] += (p[hg][0] + p[hg][1]) + (p[hg][2] + p[hg][3]);
       } else {
         const bf16x4 hi = __builtin_convertvector(p[hg], bf16x4);
-        const bf16x4 lo =
-            __builtin_convertvector(p[hg] - __builtin_convertvector(hi, f32x4), bf16x4);
         *(lds_i16x4*)(pslot((t1 & 1), hg, 0) + 8 * kh) = __builtin_bit_cast(i16x4, hi);
-        *(lds_i16x4*)(pslot((t1 & 1), hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+        if constexpr (SPLIT) {
+          const bf16x4 lo =
+              __builtin_convertvector(p[hg] - __builtin_convertvector(hi, f32x4), bf16x4);
+          *(lds_i16x4*)(pslot((t1 & 1), hg, 1) + 8 * kh) = __builtin_bit_cast(i16x4, lo);
+        }
       }
     };
     // Pieces of the softmax go after phase-2 blocks n0 + 1, n0 + 1 + kSp, ... (kSp apart).
-    constexpr int n0 = kN1;
+    constexpr int n0 = kP1;
     constexpr int kSp = (kNBH - n0 - 1) / 4 > 1 ? (kNBH - n0 - 1) / 4 : 1;
 #pragma unroll
     for (int n = n0; n < kNBH; ++n) {
@@ -474,9 +518,11 @@ void attn_fwd_pair_kernel(
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg)
         oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], phi[hg], oacc[hg][n]);
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int hg = 0; hg < 2; ++hg)
-        oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], plo[hg], oacc[hg][n]);
+        for (int hg = 0; hg < 2; ++hg)
+          oacc[hg][n] = mfma16x16x32_bf16(vf[n & 1], plo[hg], oacc[hg][n]);
+      }
       const int rel = n - n0 - 1;
       if (rel >= 0 && rel % kSp == 0 && rel / kSp < 4) piece(rel / kSp);
       __builtin_amdgcn_sched_barrier(0);
@@ -489,7 +535,7 @@ void attn_fwd_pair_kernel(
   // One pass over all tiles.  DO_PV: accumulate O and the row sums against m_ref (taken
   // from tile 0 when REF_FIRST); otherwise take the exact maximum logit of every head into
   // m_ref.  Tile t lives in LDS stage t % 3.
-  auto run_pass = [&](auto do_pv, auto ref_first) {
+  auto run_pass = [&](auto do_pv, auto ref_first, auto split) {
     constexpr bool DO_PV = decltype(do_pv)::value;
     constexpr bool REF_FIRST = decltype(ref_first)::value;
     const float zero_m[2] = {0.f, 0.f};
@@ -528,7 +574,7 @@ void attn_fwd_pair_kernel(
     if (compute) {
       if constexpr (DO_PV) {
         shifted(s, 0, m_ref, y);
-        probabilities(y, 0, l_run, ymax);
+        probabilities(y, 0, l_run, ymax, split);
       } else {
         shifted(s, 0, zero_m, y);
         ymax[0] = max4(y[0]);
@@ -540,7 +586,7 @@ void attn_fwd_pair_kernel(
     tile_barrier();  // tile 1 is in LDS; tile 0's probabilities are exchanged
     bf16x8 phi[2], plo[2];
     if constexpr (DO_PV) {
-      if (compute) read_probabilities(0, phi, plo);
+      if (compute) read_probabilities(0, phi, plo, split);
     }
     if (n_tiles > 2) Dma::issue(tiles, 2, 2, sel, n_valid, kv, ld_kv, v, ld_v);
     int st_cur = 0, st_next = 1, st_after = 2;  // stages of tiles t, t + 1, t + 2
@@ -554,7 +600,7 @@ void attn_fwd_pair_kernel(
       const int32_t row3 = Dma::row_of(t + 3, sel, n_valid);
       if (compute) {
         if constexpr (DO_PV) {
-          fused_step(st_next, st_cur, t + 1, ah, phi, plo, l_run, ymax);
+          fused_step(st_next, st_cur, t + 1, ah, phi, plo, l_run, ymax, split);
         } else {
           logits(st_next, s);
           shifted(s, t + 1, zero_m, y);
@@ -567,7 +613,7 @@ void attn_fwd_pair_kernel(
       tile_barrier();  // tile t is consumed; tile t + 2 and tile t + 1's probabilities are visible
       if constexpr (DO_PV) {
         if (compute) {
-          read_probabilities((t + 1) & 1, phi, plo);
+          read_probabilities((t + 1) & 1, phi, plo, split);
           if (t + 2 < n_tiles) read_ahead(st_after, st_next, ah);
         }
       }
@@ -578,7 +624,7 @@ void attn_fwd_pair_kernel(
       st_after = st_free;
     }
     if constexpr (DO_PV) {
-      if (compute) pv_tile(st_cur, phi, plo);  // the last tile
+      if (compute) pv_tile(st_cur, phi, plo, split);  // the last tile
     }
     // Combine the pair's halves: row sums (P.V pass) or maxima (max pass) per head.
     if (compute) {
@@ -603,14 +649,21 @@ void attn_fwd_pair_kernel(
     }
   };
 
-  if (n_tiles > 0) {
-    run_pass(std::true_type{}, std::true_type{});
+  // Block-uniform choice of the probability precision (see kSplitBelow).
+  auto forward = [&](auto split) {
+    run_pass(std::true_type{}, std::true_type{}, split);
     if (__syncthreads_or(overflow)) {
       // Rare: a logit far above tile 0's maximum.  Take the exact maximum, then redo.
-      run_pass(std::false_type{}, std::false_type{});
+      run_pass(std::false_type{}, std::false_type{}, split);
       __syncthreads();
-      run_pass(std::true_type{}, std::false_type{});
+      run_pass(std::true_type{}, std::false_type{}, split);
     }
+  };
+  if (n_tiles > 0) {
+    if (n_valid < kSplitBelow)
+      forward(std::true_type{});
+    else
+      forward(std::false_type{});
   }
 
 #pragma unroll
