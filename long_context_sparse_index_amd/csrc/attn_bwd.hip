@@ -242,17 +242,26 @@ __device__ __forceinline__ bf16x8 heads_operand(const uint16_t* x, int ld, int k
   return join_tr(lo, hi);
 }
 
-// STAGE = false: dkv [n_pools, DQK] and dv [n_pools, DV] (or nullptr: dV folded into dkv)
-// receive fp32 atomic adds.  STAGE = true: dkv and dv are staging buffers with one row per
-// (query row, slot) of this launch, row index row * k + slot, written (not added) for every
-// valid slot; dv nullptr again means dV folded into the dkv row.
-template <int DQK, int DV, bool SEPARATE_V, bool STAGE>
+// How the dK/dV kernel delivers its per-token tile results.
+enum DkvMode {
+  kDkvAtomic = 0,     // fp32 atomic adds into dkv [n_pools, DQK] (and dv [n_pools, DV], or
+                      // dV folded into dkv when dv is null)
+  kDkvStageFold = 1,  // staging rows (see below) of DQK: dK with dV added into its first DV
+  kDkvStageSplit = 2  // staging rows of DQK (dK) and, in dv, of DV (dV)
+};
+
+// Staging modes: dkv (and dv) hold one row per (query row, slot) of this launch, row index
+// row * k + slot, written (not added) for every valid slot; row `junk` receives the stores of
+// the invalid slots of a partial last tile (and, for dv, of the columns past DV), so that
+// every tile issues the same number of stores and the tile pipeline can leave them in flight.
+template <int DQK, int DV, bool SEPARATE_V, int MODE>
 __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
     const uint16_t* __restrict__ v, int64_t ld_v, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ lse, const uint16_t* __restrict__ d_o,
     const float* __restrict__ delta, float* __restrict__ dkv, float* __restrict__ dv,
-    int64_t n_pools, int h, float scale_log2, float scale) {
+    int64_t n_pools, int h, float scale_log2, float scale, int64_t junk) {
+  constexpr bool STAGE = MODE != kDkvAtomic;
   using Lds = DkvLds<DQK, DV, SEPARATE_V>;
   using Dma = typename Lds::Dma;
   constexpr int kCols = DQK / 4;     // output columns owned by each wave
@@ -324,9 +333,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
   DSA_WAIT_VMCNT(0);  // operands in registers before the tile pipeline starts
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
+  // Stores of one tile in each wave (staging modes): one 16-byte store per (row block,
+  // column block), twice with separate dV rows.
+  constexpr int kTileStores = MODE == kDkvAtomic ? 0 : 2 * kNBW * (MODE == kDkvStageSplit ? 2 : 1);
   __syncthreads();  // the staging copies are fully read before tiles overwrite them
-  Dma::for_each_tile(shared, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
-                     [&](lds_ptr tile, int t) {
+  Dma::template for_each_tile<kTileStores>(shared, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
+                                           [&](lds_ptr tile, int t) {
     const int slot0 = t * kKeysPerTile;
     TileGrads tg;
     if (wave_has_heads) {
@@ -363,14 +375,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
         for (int ks = 0; ks < 2; ++ks)
           a[arr][ks] = *reinterpret_cast<const bf16x8*>(
               &ps[arr][(mb * 16 + r16) * kPsRow + 32 * ks + 8 * g]);
-      int64_t dst[4];  // gradient row (pool), or staging row (row * k + slot); -1: none
+      if constexpr (STAGE) {
+        // Transposed products dK^T = Q^T . dS, dV^T = dO^T . P: lane (g, r) ends with columns
+        // col0 + 4 g .. col0 + 4 g + 3 of key 16 mb + r, one 16-byte store per block.
+        const int slot = slot0 + mb * 16 + r16;
+        const int64_t srow = slot < n_valid ? row * k + slot_of[slot] : junk;
+#pragma unroll
+        for (int nb = 0; nb < kNBW; ++nb) {
+          const int col0 = col_base + 16 * nb;
+          f32x4 ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            ak = mfma16x16x32_bf16(qb[nb][ks], a[2][ks], ak);
+            ak = mfma16x16x32_bf16(qb[nb][ks], a[3][ks], ak);
+          }
+          f32x4 av = {0.f, 0.f, 0.f, 0.f};
+          if (col0 < DV) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              av = mfma16x16x32_bf16(db[nb][ks], a[0][ks], av);
+              av = mfma16x16x32_bf16(db[nb][ks], a[1][ks], av);
+            }
+          }
+          const int c = col0 + 4 * g;
+          if constexpr (MODE == kDkvStageFold) {
+            *reinterpret_cast<f32x4*>(dkv + srow * DQK + c) = ak * scale + av;
+          } else {
+            *reinterpret_cast<f32x4*>(dkv + srow * DQK + c) = ak * scale;
+            const bool in_v = col0 < DV;
+            *reinterpret_cast<f32x4*>(dv + (in_v ? srow : junk) * DV + (in_v ? c : 4 * g)) = av;
+          }
+        }
+        continue;
+      }
+      int64_t dst[4];  // gradient row (pool); -1: none
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = slot0 + mb * 16 + 4 * g + i;
-        if (STAGE)
-          dst[i] = slot < n_valid ? row * k + slot_of[slot] : -1;
-        else
-          dst[i] = slot < n_valid ? sel[slot] : -1;
+        dst[i] = slot < n_valid ? sel[slot] : -1;
       }
 #pragma unroll
       for (int nb = 0; nb < kNBW; ++nb) {
@@ -395,13 +437,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
           if (dst[i] < 0) continue;
           const int64_t kat = dst[i] * DQK + col;
           const float gk = fold_v ? ak[i] * scale + (col0 < DV ? av[i] : 0.0f) : ak[i] * scale;
-          if (STAGE) {
-            dkv[kat] = gk;
-            if (!fold_v && col0 < DV) dv[dst[i] * DV + col] = av[i];
-          } else {
-            atomicAdd(dkv + kat, gk);
-            if (!fold_v && col0 < DV) atomicAdd(dv + dst[i] * DV + col, av[i]);
-          }
+          atomicAdd(dkv + kat, gk);
+          if (!fold_v && col0 < DV) atomicAdd(dv + dst[i] * DV + col, av[i]);
         }
       }
     }
@@ -420,14 +457,16 @@ size_t align256(size_t b) { return (b + 255) & ~size_t{255}; }
 
 DetLayout det_layout(int64_t rows, int k, int64_t n_pools, int d_qk, int d_v, bool separate_dv) {
   DetLayout L{};
-  const size_t pairs = static_cast<size_t>(rows > 0 ? rows : 0) * static_cast<size_t>(k);
+  // one staging row per (row, slot) pair, plus the row that takes the stores of invalid
+  // slots
+  const size_t pairs = static_cast<size_t>(rows > 0 ? rows : 0) * static_cast<size_t>(k) + 1;
   size_t off = 0;
   L.stage_k = off;
   off += align256(pairs * d_qk * sizeof(float));
   L.stage_v = off;
   if (separate_dv) off += align256(pairs * d_v * sizeof(float));
   L.reduce = off;
-  off += pool_reduce_workspace_bytes(static_cast<int64_t>(pairs), n_pools);
+  off += pool_reduce_workspace_bytes(static_cast<int64_t>(pairs - 1), n_pools);
   L.total = off;
   return L;
 }
@@ -459,10 +498,10 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!det_ws) {
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, false>),
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, kDkvAtomic>),
                        dim3(static_cast<unsigned>(nq)), dim3(kAttnThreads), 0, stream, qb, kvb,
                        ld_kv, vb, ld_v, idx, k, lse, dob, delta, dkv, dv, n_pools, h, sl2,
-                       scale);
+                       scale, int64_t{-1});
     return hipGetLastError();
   }
   // Deterministic: chunk by chunk, staged rows, then the ordered per-pool reduction.
@@ -471,13 +510,21 @@ hipError_t launch_bwd_t(const void* q, const void* kv, int64_t ld_kv, const void
   float* stage_k = reinterpret_cast<float*>(det_ws + L.stage_k);
   float* stage_v = dv ? reinterpret_cast<float*>(det_ws + L.stage_v) : nullptr;
   void* red = det_ws + L.reduce;
+  const int64_t junk = chunk * k;  // the staging row past the chunk's (row, slot) rows
   for (int64_t r0 = 0; r0 < nq; r0 += chunk) {
     const int64_t m = nq - r0 < chunk ? nq - r0 : chunk;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, true>),
-                       dim3(static_cast<unsigned>(m)), dim3(kAttnThreads), 0, stream,
-                       qb + r0 * h * DQK, kvb, ld_kv, vb, ld_v, idx + r0 * k, k, lse + r0 * h,
-                       dob + r0 * h * DV, delta + r0 * h, stage_k, stage_v, n_pools, h, sl2,
-                       scale);
+    if (dv)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, kDkvStageSplit>),
+                         dim3(static_cast<unsigned>(m)), dim3(kAttnThreads), 0, stream,
+                         qb + r0 * h * DQK, kvb, ld_kv, vb, ld_v, idx + r0 * k, k, lse + r0 * h,
+                         dob + r0 * h * DV, delta + r0 * h, stage_k, stage_v, n_pools, h, sl2,
+                         scale, junk);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<DQK, DV, SEP, kDkvStageFold>),
+                         dim3(static_cast<unsigned>(m)), dim3(kAttnThreads), 0, stream,
+                         qb + r0 * h * DQK, kvb, ld_kv, vb, ld_v, idx + r0 * k, k, lse + r0 * h,
+                         dob + r0 * h * DV, delta + r0 * h, stage_k, stage_v, n_pools, h, sl2,
+                         scale, junk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_pool_reduce(idx + r0 * k, m, k, n_pools, stage_k, DQK, dkv, stage_v, DV, dv, red,

@@ -164,21 +164,19 @@ struct TileDma {
     }
   }
 
-  // Waits for this wave's loads of a tile when `younger` later tiles may stay in flight.
-  __device__ __forceinline__ static void wait(int younger) {
-    if (younger <= 0) {
-      DSA_WAIT_VMCNT(0);
-    } else if (younger == 1) {
-      DSA_WAIT_VMCNT(kPerWave);
-    } else {
-      DSA_WAIT_VMCNT(2 * kPerWave);
-    }
+  // Waits until at most N (at most 63) vector-memory operations of this wave are pending.
+  template <int N>
+  __device__ __forceinline__ static void wait_at_most() {
+    DSA_WAIT_VMCNT(N < 63 ? N : 63);
   }
 
   // Runs body(tile, t) for every tile t in order with DEPTH - 1 tiles prefetched; `tile` is
   // an LDS pointer to the tile.
-  // All threads of the block must call it (it contains barriers).
-  template <class Body>
+  // All threads of the block must call it (it contains barriers).  kBodyOps: the number of
+  // vector-memory operations (e.g. stores) every call of body issues in each wave, exactly;
+  // those issued after a tile's loads are allowed to stay in flight while the pipeline waits
+  // for that tile (vector-memory operations complete in issue order for the wait counter).
+  template <int kBodyOps = 0, class Body>
   __device__ __forceinline__ static void for_each_tile(uint8_t* tiles, int n_tiles,
                                                        const int32_t* sel, int n_valid,
                                                        const uint16_t* __restrict__ kv,
@@ -197,8 +195,26 @@ struct TileDma {
       for (int s = 0; s < DEPTH - 1 && s < n_tiles; ++s)
         issue(tiles, s, s, sel, n_valid, kv, ld_kv, v, ld_v);
       for (int t = 0; t < n_tiles; ++t) {
-        const int ahead = n_tiles - 1 - t;
-        wait(ahead < DEPTH - 2 ? ahead : DEPTH - 2);
+        // Operations issued after tile t's loads: with DEPTH 3, tile t + 1's loads (issued at
+        // iteration t - 1, if that tile exists) and the bodies of tiles t - 2 and t - 1; with
+        // DEPTH 2, the body of tile t - 1.  (The memory clobber keeps the previous body's
+        // stores ahead of the wait, where the count assumes them.)
+        asm volatile("" ::: "memory");
+        if constexpr (DEPTH == 2) {
+          if (t == 0)
+            wait_at_most<0>();
+          else
+            wait_at_most<kBodyOps>();
+        } else {
+          const bool next = t + 1 < n_tiles;
+          if (t == 0) {
+            if (next) wait_at_most<kPerWave>(); else wait_at_most<0>();
+          } else if (t == 1) {
+            if (next) wait_at_most<kPerWave + kBodyOps>(); else wait_at_most<kBodyOps>();
+          } else {
+            if (next) wait_at_most<kPerWave + 2 * kBodyOps>(); else wait_at_most<2 * kBodyOps>();
+          }
+        }
         tile_barrier();  // tile t is in LDS for every wave; tile t-1 is consumed
         if (t + DEPTH - 1 < n_tiles)
           issue(tiles, (t + DEPTH - 1) % DEPTH, t + DEPTH - 1, sel, n_valid, kv, ld_kv, v,

@@ -76,31 +76,54 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
   }
 }
 
-// Exclusive prefix sum of a[0 .. n) in place, by one workgroup of 1024 threads (each thread
-// one contiguous segment).
+// Exclusive prefix sum of a[0 .. n) in place, by one workgroup of 1024 threads, in rounds
+// of 16384 entries: a coalesced load into LDS, a sequential sum of 16 consecutive entries per
+// thread, a block scan of those sums, the sequential rewrite, a coalesced store.
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;
+constexpr int kScanRound = kScanThreads * kScanPer;
+__device__ __forceinline__ int scan_slot(int e) { return (e / kScanPer) * (kScanPer + 1) + e % kScanPer; }
+
 __global__ __launch_bounds__(kScanThreads) void exclusive_scan_kernel(uint32_t* __restrict__ a,
                                                                       int64_t n) {
+  __shared__ uint32_t buf[kScanThreads * (kScanPer + 1)];  // padded: no bank conflicts
   __shared__ uint32_t part[kScanThreads];
   const int tid = threadIdx.x;
-  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = tid * per;
-  const int64_t hi = lo + per < n ? lo + per : n;
-  uint32_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += a[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int d = 1; d < kScanThreads; d <<= 1) {
-    const uint32_t v = tid >= d ? part[tid - d] : 0u;
+  uint32_t carry = 0;
+  for (int64_t base = 0; base < n; base += kScanRound) {
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int e = j * kScanThreads + tid;
+      buf[scan_slot(e)] = base + e < n ? a[base + e] : 0u;
+    }
     __syncthreads();
-    part[tid] += v;
+    uint32_t* mine = buf + tid * (kScanPer + 1);
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) s += mine[j];
+    part[tid] = s;
     __syncthreads();
-  }
-  uint32_t run = part[tid] - s;  // exclusive offset of this segment
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint32_t v = a[i];
-    a[i] = run;
-    run += v;
+    for (int d = 1; d < kScanThreads; d <<= 1) {
+      const uint32_t v = tid >= d ? part[tid - d] : 0u;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    uint32_t run = carry + part[tid] - s;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const uint32_t v = mine[j];
+      mine[j] = run;
+      run += v;
+    }
+    carry += part[kScanThreads - 1];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int e = j * kScanThreads + tid;
+      if (base + e < n) a[base + e] = buf[scan_slot(e)];
+    }
+    __syncthreads();
   }
 }
 
@@ -173,16 +196,23 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 }
 
 // seg[s] = first sorted position of pool s (s in [0, n_pools]); pool s's entries are
-// [seg[s], seg[s + 1]).  Keys are sorted, with n_pools marking empty slots at the end.
+// [seg[s], seg[s + 1]).  Keys are sorted, with n_pools marking empty slots at the end.  Each
+// thread looks at 16 consecutive positions i (and position n, past the end, closes the list).
+constexpr int kBoundsPer = 16;
 __global__ __launch_bounds__(256) void segment_bounds_kernel(const int32_t* __restrict__ keys,
                                                              int64_t n, int32_t n_pools,
                                                              int32_t* __restrict__ seg) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i > n) return;
-  const int64_t prev = i == 0 ? -1 : keys[i - 1];
-  const int64_t cur = i == n ? static_cast<int64_t>(n_pools) + 1 : keys[i];
-  const int64_t top = cur < n_pools ? cur : n_pools;
-  for (int64_t s = prev + 1; s <= top; ++s) seg[s] = static_cast<int32_t>(i);
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kBoundsPer;
+  if (i0 > n) return;
+  int64_t prev = i0 == 0 ? -1 : keys[i0 - 1];
+  for (int j = 0; j < kBoundsPer; ++j) {
+    const int64_t i = i0 + j;
+    const int64_t cur = i == n ? static_cast<int64_t>(n_pools) + 1 : keys[i];
+    const int64_t top = cur < n_pools ? cur : n_pools;
+    for (int64_t s = prev + 1; s <= top; ++s) seg[s] = static_cast<int32_t>(i);
+    if (i == n) break;
+    prev = cur;
+  }
 }
 
 // out[s, :] += sum over the pool's sorted entries e of stage[e, :], in sorted order.  One
@@ -317,8 +347,10 @@ hipError_t launch_pool_reduce(const int32_t* idx, int64_t rows, int k, int64_t n
     if (e != hipSuccess) return e;
     cur = nxt;
   }
-  hipLaunchKernelGGL(segment_bounds_kernel, dim3(static_cast<unsigned>((n + 1 + 255) / 256)),
-                     dim3(256), 0, s, keys[cur], n, np, seg);
+  const int64_t bound_threads = n / kBoundsPer + 1;  // thread n / 16 holds position n
+  hipLaunchKernelGGL(segment_bounds_kernel,
+                     dim3(static_cast<unsigned>((bound_threads + 255) / 256)), dim3(256), 0, s,
+                     keys[cur], n, np, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_reduce(w_k, seg, vals[cur], n, stage_k, out_k, n_pools, s);
