@@ -115,7 +115,7 @@ __device__ __forceinline__ void tile_grads(lds_ptr tile, const bf16x8* qf,
             lds_load_bf16x8(tile + tile_off(VBASE + 4 * ks + g, mb * 16 + r16)), dof[ks],
             dp[mb]);
   }
-  i16x8 ph, pl, sh, sl;
+  f32x8 pv, dv;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -125,17 +125,12 @@ __device__ __forceinline__ void tile_grads(lds_ptr tile, const bf16x8* qf,
       const float d = p * (dp[mb][i] - dh);
       out.p[mb][i] = p;
       out.ds[mb][i] = d;
-      const uint16_t phb = float_to_bf16_bits(p);
-      const uint16_t shb = float_to_bf16_bits(d);
-      ph[mb * 4 + i] = static_cast<short>(phb);
-      pl[mb * 4 + i] = static_cast<short>(float_to_bf16_bits(p - bf16_bits_to_float(phb)));
-      sh[mb * 4 + i] = static_cast<short>(shb);
-      sl[mb * 4 + i] = static_cast<short>(float_to_bf16_bits(d - bf16_bits_to_float(shb)));
+      pv[mb * 4 + i] = p;
+      dv[mb * 4 + i] = d;
     }
-  out.p_hi = bf16x8_from_bits(ph);
-  out.p_lo = bf16x8_from_bits(pl);
-  out.ds_hi = bf16x8_from_bits(sh);
-  out.ds_lo = bf16x8_from_bits(sl);
+  // hi = RNE(x), lo = RNE(x - hi) with the hardware packed conversion
+  split_bf16x8(pv, out.p_hi, out.p_lo);
+  split_bf16x8(dv, out.ds_hi, out.ds_lo);
 }
 
 // The wave's B operands for S^T (queries) and dP^T (dO): lane column = head.
@@ -351,18 +346,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dkv_kernel(
         for (int i = 0; i < 4; ++i) tg.p[mb][i] = tg.ds[mb][i] = 0.0f;
     }
     // P^T and dS^T of this wave's heads into the [key][head] arrays (hi, lo parts).
+    {
+      f32x8 pv, dv8;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int at = (mb * 16 + 4 * g + i) * kPsRow + head;
-        const float p = tg.p[mb][i], d = tg.ds[mb][i];
-        const uint16_t phb = float_to_bf16_bits(p), shb = float_to_bf16_bits(d);
-        ps[0][at] = phb;
-        ps[1][at] = float_to_bf16_bits(p - bf16_bits_to_float(phb));
-        ps[2][at] = shb;
-        ps[3][at] = float_to_bf16_bits(d - bf16_bits_to_float(shb));
+        for (int i = 0; i < 4; ++i) pv[mb * 4 + i] = tg.p[mb][i], dv8[mb * 4 + i] = tg.ds[mb][i];
+      bf16x8 parts[4];
+      split_bf16x8(pv, parts[0], parts[1]);
+      split_bf16x8(dv8, parts[2], parts[3]);
+#pragma unroll
+      for (int arr = 0; arr < 4; ++arr) {
+        const i16x8 bits = __builtin_bit_cast(i16x8, parts[arr]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ps[arr][(mb * 16 + 4 * g + i) * kPsRow + head] =
+                static_cast<uint16_t>(bits[mb * 4 + i]);
       }
+    }
     DSA_WAIT_LGKMCNT0();
     tile_barrier();
     // This wave's columns of dK_tile = dS^T . Q and dV_tile = P^T . dO (64-head contraction).

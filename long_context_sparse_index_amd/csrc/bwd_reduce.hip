@@ -11,7 +11,7 @@
 //      digit radix sort of the chunk's selection entries by pool, 4 bits per pass, whose
 //      input order is the pairs' own order (row-major, slot-minor), so each pool's pairs come
 //      out in that order whatever the thread timing;
-//   2. segment bounds: the first sorted position of every pool;
+//   2. segment bounds: the first sorted position of every pool (binary search);
 //   3. one workgroup per pool adds its staging rows in the sorted order (one fp32 sum per
 //      column, sequential) and adds the result to the pool's gradient row (read-modify-write:
 //      no other workgroup touches that row).
@@ -196,23 +196,22 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 }
 
 // seg[s] = first sorted position of pool s (s in [0, n_pools]); pool s's entries are
-// [seg[s], seg[s + 1]).  Keys are sorted, with n_pools marking empty slots at the end.  Each
-// thread looks at 16 consecutive positions i (and position n, past the end, closes the list).
-constexpr int kBoundsPer = 16;
+// [seg[s], seg[s + 1]).  Keys are sorted, with n_pools marking empty slots at the end: one
+// thread per pool finds the first key >= s by binary search.
 __global__ __launch_bounds__(256) void segment_bounds_kernel(const int32_t* __restrict__ keys,
                                                              int64_t n, int32_t n_pools,
                                                              int32_t* __restrict__ seg) {
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kBoundsPer;
-  if (i0 > n) return;
-  int64_t prev = i0 == 0 ? -1 : keys[i0 - 1];
-  for (int j = 0; j < kBoundsPer; ++j) {
-    const int64_t i = i0 + j;
-    const int64_t cur = i == n ? static_cast<int64_t>(n_pools) + 1 : keys[i];
-    const int64_t top = cur < n_pools ? cur : n_pools;
-    for (int64_t s = prev + 1; s <= top; ++s) seg[s] = static_cast<int32_t>(i);
-    if (i == n) break;
-    prev = cur;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (s > n_pools) return;
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (keys[mid] < s)
+      lo = mid + 1;
+    else
+      hi = mid;
   }
+  seg[s] = static_cast<int32_t>(lo);
 }
 
 // out[s, :] += sum over the pool's sorted entries e of stage[e, :], in sorted order.  One
@@ -347,10 +346,8 @@ hipError_t launch_pool_reduce(const int32_t* idx, int64_t rows, int k, int64_t n
     if (e != hipSuccess) return e;
     cur = nxt;
   }
-  const int64_t bound_threads = n / kBoundsPer + 1;  // thread n / 16 holds position n
-  hipLaunchKernelGGL(segment_bounds_kernel,
-                     dim3(static_cast<unsigned>((bound_threads + 255) / 256)), dim3(256), 0, s,
-                     keys[cur], n, np, seg);
+  hipLaunchKernelGGL(segment_bounds_kernel, dim3(static_cast<unsigned>((n_pools + 1 + 255) / 256)),
+                     dim3(256), 0, s, keys[cur], n, np, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_reduce(w_k, seg, vals[cur], n, stage_k, out_k, n_pools, s);
