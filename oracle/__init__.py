@@ -11,6 +11,8 @@ from .oracle import (  # noqa: F401
     decode_e4m3,
     index_scores,
     library_path,
+    pool_keys,
+    round_bf16,
     sparse_attn_bwd,
     sparse_attn_fwd,
     topk,

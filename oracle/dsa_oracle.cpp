@@ -22,7 +22,9 @@
 //  * sparse attention is softmax(scale * q . K[idx]) applied to V[idx] per query head, all
 //    heads sharing one latent KV row; V is the first d_v columns of that row unless a
 //    separate V table is given; a row with no valid slot gives O = 0 and LSE = -inf;
-//  * the backward pass is the exact gradient of that attention in the valid slots.
+//  * the backward pass is the exact gradient of that attention in the valid slots;
+//  * a pooled key is the average of its 4 tokens' rows weighted by the softmax of their gate
+//    scores (the pages name "k-pool gate scores" but print no formula).
 //
 // Arithmetic: plain loops in double precision, one rounding at the output where the output
 // has a storage type (indexer scores are rounded once to fp32).  Every entry point takes an
@@ -403,6 +405,70 @@ int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv, int64_t ld
   const AttnArgs a{qd.data(), kvd.data(), ld_kv, v ? vd.data() : nullptr, ld_v, idx, k,
                    nrows, n_pools, h, d_qk, d_v, scale};
   return attn_bwd(a, dod.data(), dq, dk, dv, nthreads);
+}
+
+// ---------------------------------------------------------------------------------------
+// Pooled keys ("one pool per 4 tokens", page "SkyRL extends GLM-5.3-Flash training context to
+// 1 million tokens", section "Model and bottleneck"; pooling by "k-pool gate scores", section
+// "Four optimizations", item 3).  The pages print no formula; the reading taken: pool s is
+// the average of the rows of tokens 4s .. 4s+3 weighted by the softmax of their gate scores,
+//     w_i = exp(g[4s+i]) / sum_j exp(g[4s+j]),   pooled[s, :] = sum_i w_i x[4s+i, :],
+// for s < floor(n_tokens / 4) (a trailing partial pool is never visible, so never formed),
+// rounded once to bf16 (round to nearest, ties to even).
+
+namespace {
+
+// The bf16 value nearest to v (ties to an even last mantissa bit), as its 16-bit pattern,
+// rounded from the double directly (no intermediate float rounding).  Finite v of bf16
+// range only.
+uint16_t round_to_bf16(double v) {
+  if (v == 0.0) return std::signbit(v) ? 0x8000 : 0x0000;
+  const bool neg = v < 0.0;
+  const double a = neg ? -v : v;
+  int e;
+  (void)std::frexp(a, &e);  // a = m * 2^e with m in [0.5, 1)
+  // bf16 keeps 8 significant bits for normal numbers (exponent e >= -125, i.e. a >= 2^-126);
+  // below that the spacing stays 2^-133 (subnormals).
+  const int shift = e >= -125 ? 8 - e : 133;
+  const double r = std::nearbyint(std::ldexp(a, shift));  // default mode: ties to even
+  const float f = static_cast<float>(std::ldexp(r, -shift));  // exact: 8 bits at most
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  return static_cast<uint16_t>((u >> 16) | (neg ? 0x8000u : 0u));
+}
+
+}  // namespace
+
+void dsa_oracle_round_bf16(const double* src, uint16_t* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = round_to_bf16(src[i]);
+}
+
+// x: [n_tokens, ld_x] bf16 bits (the first d columns are pooled); gate: [n_tokens] fp32.
+// out_f64 (optional): [n_pools, d] the pooled values before rounding; out_bits: [n_pools, d]
+// bf16 bits.  n_pools = floor(n_tokens / 4).
+int dsa_oracle_pool_keys(const uint16_t* x, int64_t ld_x, const float* gate, int64_t n_tokens,
+                         int d, double* out_f64, uint16_t* out_bits, int nthreads) {
+  if (!x || !gate || !out_bits || n_tokens < 0 || d <= 0 || ld_x < d) return -1;
+  const int64_t n_pools = n_tokens / 4;
+  parallel_rows(n_pools, nthreads, [&](int64_t s, int) {
+    double g[4], m = -std::numeric_limits<double>::infinity();
+    for (int i = 0; i < 4; ++i) {
+      g[i] = static_cast<double>(gate[4 * s + i]);
+      m = std::max(m, g[i]);
+    }
+    double wsum = 0.0, w[4];
+    for (int i = 0; i < 4; ++i) {
+      w[i] = std::exp(g[i] - m);
+      wsum += w[i];
+    }
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int i = 0; i < 4; ++i) acc += (w[i] / wsum) * decode_bf16(x[(4 * s + i) * ld_x + c]);
+      if (out_f64) out_f64[s * d + c] = acc;
+      out_bits[s * d + c] = round_to_bf16(acc);
+    }
+  });
+  return 0;
 }
 
 }  // extern "C"

@@ -60,6 +60,8 @@ def _load():
             lib.dsa_oracle_sparse_attn_bwd.argtypes = [
                 _P, _P, _I64, _P, _I64, _P, _INT, _P, _I64, _I64, _INT, _INT, _INT, _DBL, _P,
                 _P, _P, _INT]
+            lib.dsa_oracle_round_bf16.argtypes = [_P, _P, _I64]
+            lib.dsa_oracle_pool_keys.argtypes = [_P, _I64, _P, _I64, _INT, _P, _P, _INT]
             lib.dsa_oracle_sparse_attn_fwd_f64.argtypes = lib.dsa_oracle_sparse_attn_fwd.argtypes
             lib.dsa_oracle_sparse_attn_bwd_f64.argtypes = lib.dsa_oracle_sparse_attn_bwd.argtypes
             _lib = lib
@@ -190,3 +192,28 @@ def sparse_attn_bwd(q_bits, kv_bits, idx, do_bits, scale, *, v_bits=None, d_v=No
         nrows, n_pools, h, d_qk, d_v, float(scale), _ptr(dq), _ptr(dk), _ptr(dv), threads)
     _check(rc, "sparse_attn_bwd")
     return dq, dk, dv
+
+
+def round_bf16(values) -> np.ndarray:
+    """Nearest bf16 (ties to even) of each float64 value, as uint16 bit patterns."""
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(values.shape, dtype=np.uint16)
+    _load().dsa_oracle_round_bf16(_ptr(values), _ptr(out), values.size)
+    return out
+
+
+def pool_keys(x_bits, gate, *, threads: int = 0):
+    """Pooled keys of floor(n / 4) pools: (float64 values before rounding, bf16 bits).
+
+    x_bits [n, ld] uint16 bf16 bits (all ld columns pooled), gate float32 [n]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    n, d = x_bits.shape
+    assert gate.shape == (n,)
+    p = n // 4
+    f64 = np.empty((p, d), dtype=np.float64)
+    bits = np.empty((p, d), dtype=np.uint16)
+    rc = _load().dsa_oracle_pool_keys(_ptr(x_bits), d, _ptr(gate), n, d, _ptr(f64), _ptr(bits),
+                                      threads)
+    _check(rc, "pool_keys")
+    return f64, bits

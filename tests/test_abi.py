@@ -133,7 +133,8 @@ def test_fused_select_and_deterministic_workspaces(lib):
                                                                   1)
     pairs = 100 * 2048
     assert det >= base + pairs * 576 * 4 + 4 * pairs * 4 + 5001 * 4
-    assert det_v - det == pairs * 512 * 4
+    # (one more staging row takes the stores of invalid slots)
+    assert det_v - det == ((pairs + 1) * 512 * 4 + 255) // 256 * 256
     # chunks of 4096 rows: the staging does not grow past them
     big = lib.dsa_sparse_attn_bwd_deterministic_workspace_bytes(65536, 64, 16384, 2048, 576,
                                                                 512, 0)
