@@ -331,6 +331,9 @@ def measure(wl, steps, warmup, args, dev):
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                 "traffic": recorded_traffic("attn_fwd", wl.name)}
 
+    if has_attn:
+        phases["pool_keys"] = time_pool_keys(wl, dev, stream)
+
     if has_attn and "attn_bwd" in wl.phases:
         idx_b = idx_for_bwd(wl, q_i, k_i, w, dev)
         phases["attn_bwd"] = time_backward(wl, q, kv, o, lse, idx_b, steps, stream)
@@ -372,6 +375,38 @@ def measure(wl, steps, warmup, args, dev):
         "cpu_baseline": cpu,
     }
     return line
+
+
+def time_pool_keys(wl, dev, stream, reps=20):
+    """dsa_pool_keys on token-level latent rows of the workload ([N, d_qk] bf16 and N gate
+    scores -> [N / 4, d_qk]), the step upstream of the chunked forward that forms its pooled
+    keys (the forward's inputs are pooled already, so this is timed on its own)."""
+    import torch
+
+    from long_context_sparse_index_amd import binding as B
+    from long_context_sparse_index_amd import inputs as I
+
+    n, d = wl.n_tokens, wl.d_qk
+    x = I.normal_bf16((n, d), 0, "kv", dev)
+    gate = I.normal_bf16((n,), 0, "d_o", dev).float().contiguous()
+    out = torch.empty((n // 4, d), dtype=torch.bfloat16, device=dev)
+    B.pool_keys(x, gate, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.pool_keys(x, gate, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = n * d * 2 + n * 4 + (n // 4) * d * 2
+    del x, gate, out
+    return {"ms_per_call": ms, "bytes_per_call": nbytes,
+            "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "note": "dsa_pool_keys of %d token rows of %d bf16 columns (not part of the step: "
+                    "the forward's key tables are pooled already), %d calls" % (n, d, reps)}
 
 
 def idx_for_bwd(wl, q_i, k_i, w, dev):

@@ -256,6 +256,25 @@ size_t dsa_sparse_attn_bwd_deterministic_workspace_bytes(int64_t nq, int32_t h,
                                                          int32_t separate_dv);
 
 /*
+ * dsa_pool_keys - pooled key rows, one per 4 tokens, from per-token rows and gate scores.
+ * Source: page "SkyRL ... 1 million tokens", section "Model and bottleneck" (the indexer
+ * scores "one pool per 4 tokens") and section "Four optimizations", item 3 (pools are formed
+ * with "k-pool gate scores").  The pages print no formula; the reading implemented: pool s is
+ * the average of the rows of tokens 4s .. 4s+3 weighted by the softmax of their gate scores,
+ *     out[s, c] = sum_{i<4} softmax(gate[4s .. 4s+3])_i * x[4s+i, c],
+ * for s < floor(n_tokens / 4) (a partial last pool is never visible to any query, since pool
+ * s becomes visible at token 4s+3, so it is not formed).  The same call pools any bf16 key
+ * table: the indexer keys (d = d_i) and the latent KV rows (d = 576).
+ *   x     [n_tokens, ld_x] bf16 (columns [0, d) are pooled);  gate [n_tokens] fp32.
+ *   out   [n_tokens / 4, ld_out] bf16 output (columns [0, d) written).
+ *   Supported: d a multiple of 8; ld_x, ld_out multiples of 8 (>= d); x, out 16-byte aligned.
+ *   With n_tokens < 4 no pool is formed, nothing is accessed and the pointers may be NULL.
+ * Arithmetic: fp32 softmax and weighted sum, one rounding to bf16 (nearest, ties to even).
+ */
+dsa_status dsa_pool_keys(const void* x, int64_t ld_x, const float* gate, int64_t n_tokens,
+                         int32_t d, void* out, int64_t ld_out, void* stream);
+
+/*
  * dsa_forward_chunked - the whole DSA forward over n_tokens queries, one query chunk at a
  * time: for each chunk [t0, t0 + chunk) it runs the select (dsa_index_topk when k <= 2730,
  * else dsa_index_scores into one reused fp32 score buffer in the workspace and dsa_topk),

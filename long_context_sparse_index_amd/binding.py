@@ -68,6 +68,7 @@ _SIGNATURES = {
     "dsa_index_topk": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                         _P, _P, _SZ, _P], ctypes.c_int),
     "dsa_index_topk_workspace_bytes": ([_I64, _I64, _I32], _SZ),
+    "dsa_pool_keys": ([_P, _I64, _P, _I64, _I32, _P, _I64, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -313,6 +314,21 @@ def forward_chunked(q_idx, k_idx, w, q, kv, o, lse, *, k: int, chunk: int, scale
         ws.numel() * ws.element_size(),
         _stream(stream)))
     return o, lse, idx_out
+
+
+def pool_keys(x, gate, out, *, stream=None):
+    """out[s] = softmax(gate[4s:4s+4]) . x[4s:4s+4] in bf16, for s < x.shape[0] // 4.
+
+    x [n_tokens, d] bf16 (row stride may exceed d), gate [n_tokens] fp32,
+    out [n_tokens // 4, d] bf16."""
+    n, d = x.shape
+    assert x.dtype == torch.bfloat16 and out.dtype == torch.bfloat16
+    assert gate.dtype == torch.float32 and gate.is_contiguous() and gate.shape == (n,)
+    assert x.stride(1) == 1 and out.stride(1) == 1 and out.shape == (n // 4, d)
+    lib = load_library()
+    _check(lib.dsa_pool_keys(_ptr(x), x.stride(0), _ptr(gate), n, d, _ptr(out), out.stride(0),
+                             _stream(stream)))
+    return out
 
 
 # ----------------------------------------------------------------- allocating conveniences

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "bwd_reduce.hip"]
+           "bwd_reduce.hip", "pool.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -397,6 +397,21 @@ dsa_status dsa_sparse_attn_bwd_deterministic(
                     "dsa_sparse_attn_bwd_deterministic launch");
 }
 
+dsa_status dsa_pool_keys(const void* x, int64_t ld_x, const float* gate, int64_t n_tokens,
+                         int32_t d, void* out, int64_t ld_out, void* stream) {
+  DSA_REQUIRE(n_tokens >= 0, "pool_keys: n_tokens must be >= 0");
+  DSA_REQUIRE((x && gate && out) || n_tokens < 4, "pool_keys: null x, gate or out");
+  DSA_REQUIRE(d >= 1, "pool_keys: d must be >= 1");
+  if (d % 8 != 0) return fail(DSA_ERR_UNSUPPORTED, "pool_keys: d = %d is not a multiple of 8", d);
+  DSA_REQUIRE(ld_x >= d && ld_out >= d && ld_x % 8 == 0 && ld_out % 8 == 0,
+              "pool_keys: ld_x and ld_out must be >= d and multiples of 8");
+  DSA_REQUIRE(aligned(x, 16) && aligned(out, 16) && aligned(gate, 4),
+              "pool_keys: x and out must be 16-byte aligned, gate 4-byte aligned");
+  return hip_status(dsa::launch_pool_keys(x, ld_x, gate, n_tokens, d, out, ld_out,
+                                          static_cast<hipStream_t>(stream)),
+                    "dsa_pool_keys launch");
+}
+
 size_t dsa_index_topk_workspace_bytes(int64_t nq, int64_t n_pools, int32_t k) {
   if (nq <= 0 || k <= 0 || n_pools < 0) return 0;
   return fused_layout(nq, n_pools).total;

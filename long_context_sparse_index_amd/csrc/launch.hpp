@@ -95,4 +95,10 @@ hipError_t launch_pool_reduce(const int32_t* idx, int64_t rows, int k, int64_t n
                               const float* stage_v, int w_v, float* out_v, void* ws,
                               hipStream_t s);
 
+// Pooled keys (pool.hip): out[s, :d] = the gate-softmax-weighted average of rows 4s .. 4s+3
+// of x, for s < n_tokens / 4, in bf16.  d a multiple of 8; x, out 16-byte aligned with row
+// strides (elements) multiples of 8.
+hipError_t launch_pool_keys(const void* x, int64_t ld_x, const float* gate, int64_t n_tokens,
+                            int d, void* out, int64_t ld_out, hipStream_t stream);
+
 }  // namespace dsa

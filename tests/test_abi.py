@@ -189,3 +189,13 @@ def test_noalloc_backward_rejects_sizes_past_its_static_scratch(lib):
               4, 100, 64, 576, 512, 0.1, None) == 1
     assert nb(FAKE, FAKE, 576, None, 0, FAKE, 2048, FAKE, F32, FAKE, FAKE, FAKE, FAKE, None,
               -1, 100, 64, 576, 512, 0.1, None) == 1
+
+
+def test_pool_keys_rejects_bad_arguments(lib):
+    pk = lib.dsa_pool_keys
+    assert pk(None, 64, FAKE, 16, 64, FAKE, 64, None) == 1
+    assert pk(None, 64, None, 3, 64, None, 64, None) == 0  # no pool: nothing accessed
+    assert pk(FAKE, 64, FAKE, 16, 60, FAKE, 64, None) == 2  # d not a multiple of 8
+    assert pk(FAKE, 56, FAKE, 16, 64, FAKE, 64, None) == 1  # ld_x < d
+    assert pk(FAKE, 64, FAKE, -1, 64, FAKE, 64, None) == 1
+    assert pk(P(0x10008), 64, FAKE, 16, 64, FAKE, 64, None) == 1  # misaligned x
