@@ -10,8 +10,9 @@
 //   1. delta: D[t, h] = dO[t, h, :] . O[t, h, :], one wave per (token, head) row.
 //   2. dq: per token, one wave per 16 heads, over 32-key tiles of the gathered latent rows:
 //      recompute S^T and P^T as the forward does, dP^T = V_tile . dO^T (A: value rows from
-//      LDS, B: the wave's dO, held in registers), dS^T in registers, and
-//      dQ^T += K_tile^T . dS^T with K^T from LDS transpose reads; dQ stays in registers.
+//      LDS, B: the wave's dO, held in registers) and dS^T in registers; dS^T of all heads is
+//      exchanged through LDS and each wave accumulates dQ^T += K_tile^T . dS^T for a quarter
+//      of the columns and all heads, K^T from LDS transpose reads; dQ stays in registers.
 //   3. dkv: per token, the same recomputation, then P^T and dS^T of all 64 heads go to LDS
 //      and each wave forms its quarter of the tile's columns of
 //          dK_tile = dS^T . Q (contraction over the 64 heads),  dV_tile = P^T . dO
@@ -150,6 +151,17 @@ __device__ __forceinline__ void load_head_operands(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- 2. dQ
+// dS^T of all heads is exchanged through LDS so that each wave forms a quarter of the columns
+// of dQ^T = K^T . dS^T for all heads: every transposed key block is read by one wave instead
+// of four.  Exchange layout: [hi/lo][head][position] bf16 with the tile's keys at position
+// 8 g + 4 mb + i for key 16 mb + 4 g + i (the operand slot order of lane group g), so a lane
+// writes its 8 values with one 16-byte store and reads an operand with one 16-byte load;
+// rows of 40 bf16 (80 bytes) keep the 16 lanes of a group on distinct banks.  Two buffers
+// alternate between tiles.
+constexpr int kDsRow = 40;
+constexpr int kDsBuf = 2 * 64 * kDsRow;  // bf16 per buffer (hi and lo)
+constexpr int kDqXchgBytes = 2 * kDsBuf * 2;
+
 template <int DQK, int DV, bool SEPARATE_V>
 __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t ld_kv,
@@ -158,9 +170,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
     const float* __restrict__ delta, float* __restrict__ dq, int64_t n_pools, int h,
     float scale_log2, float scale) {
   constexpr int kTileBytes = TileDma<DQK, DV, SEPARATE_V, 1>::kTileBytes;
-  using Dma = TileDma<DQK, DV, SEPARATE_V, pick_depth(kTileBytes, kMaxTopK * 4 + 64)>;
-  constexpr int kNQ = DQK / 16;
+  using Dma = TileDma<DQK, DV, SEPARATE_V,
+                      pick_depth(kTileBytes, kMaxTopK * 4 + 64 + kDqXchgBytes)>;
+  constexpr int kNBW = DQK / 64;  // 16-column blocks of dQ per wave (a quarter of DQK)
+  static_assert(DQK % 64 == 0, "column quarters of whole 16-column blocks");
   __shared__ __attribute__((aligned(16))) uint8_t tiles[Dma::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t dsx[2 * kDsBuf];
   __shared__ int32_t sel[kMaxTopK];
   __shared__ int wave_tmp[kAttnThreads / 64];
 
@@ -172,6 +187,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
   const int head = wid * 16 + r16;
   const bool head_ok = head < h;
   const bool wave_has_heads = wid * 16 < h;
+  const int nb0 = wid * kNBW;  // this wave's first column block
 
   const int n_valid = compact_selection(idx + row * k, k, n_pools, sel, wave_tmp);
   bf16x8 qf[DQK / 32], dof[DV / 32];
@@ -180,31 +196,56 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_dq_kernel(
   const float dh = head_ok ? delta[row * h + head] : 0.0f;
   DSA_WAIT_VMCNT(0);  // operands in registers before the tile pipeline starts
 
-  f32x4 acc[kNQ];
+  f32x4 acc[4][kNBW];  // [head block][column block]
 #pragma unroll
-  for (int nb = 0; nb < kNQ; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb) acc[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_tiles = (n_valid + kKeysPerTile - 1) / kKeysPerTile;
   Dma::for_each_tile(tiles, n_tiles, sel, n_valid, kv, ld_kv, v, ld_v,
                      [&](lds_ptr tile, int t) {
-    if (!wave_has_heads) return;
-    TileGrads tg;
-    tile_grads<DQK, DV, Dma::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
-                                     scale_log2, lse2, dh, g, r16, tg);
-    // dQ^T += K^T . dS^T over the tile's keys.
+    uint16_t* const xb = dsx + (t & 1) * kDsBuf;
+    bf16x8 ds_hi = bf16x8_zero(), ds_lo = bf16x8_zero();
+    if (wave_has_heads) {
+      TileGrads tg;
+      tile_grads<DQK, DV, Dma::kVBase>(tile, qf, dof, t * kKeysPerTile, n_valid, head_ok,
+                                       scale_log2, lse2, dh, g, r16, tg);
+      ds_hi = tg.ds_hi;
+      ds_lo = tg.ds_lo;
+    }
+    *reinterpret_cast<bf16x8*>(xb + head * kDsRow + 8 * g) = ds_hi;
+    *reinterpret_cast<bf16x8*>(xb + 64 * kDsRow + head * kDsRow + 8 * g) = ds_lo;
+    DSA_WAIT_LGKMCNT0();
+    tile_barrier();  // every head's dS^T of tile t is in the exchange buffer
+    bf16x8 b_hi[4], b_lo[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      b_hi[hb] = *reinterpret_cast<const bf16x8*>(xb + (hb * 16 + r16) * kDsRow + 8 * g);
+      b_lo[hb] =
+          *reinterpret_cast<const bf16x8*>(xb + 64 * kDsRow + (hb * 16 + r16) * kDsRow + 8 * g);
+    }
+    // dQ^T += K^T . dS^T over the tile's keys, this wave's columns, all heads.
     const lds_ptr kt_base = tile + tile_tr_lane_off(0, g, r16);
 #pragma unroll
-    for (int nb = 0; nb < kNQ; ++nb) {
-      const bf16x8 kt = tile_tr_block(kt_base, nb);
-      acc[nb] = mfma16x16x32_bf16(kt, tg.ds_hi, acc[nb]);
-      acc[nb] = mfma16x16x32_bf16(kt, tg.ds_lo, acc[nb]);
+    for (int nb = 0; nb < kNBW; ++nb) {
+      const bf16x8 kt = tile_tr_block(kt_base, nb0 + nb);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        acc[hb][nb] = mfma16x16x32_bf16(kt, b_hi[hb], acc[hb][nb]);
+        acc[hb][nb] = mfma16x16x32_bf16(kt, b_lo[hb], acc[hb][nb]);
+      }
     }
   });
-  if (!head_ok) return;
-  float* out = dq + (row * h + head) * DQK;
 #pragma unroll
-  for (int nb = 0; nb < kNQ; ++nb)
-    *reinterpret_cast<f32x4*>(out + nb * 16 + 4 * g) = acc[nb] * scale;
+  for (int hb = 0; hb < 4; ++hb) {
+    const int hh = hb * 16 + r16;
+    if (hh >= h) continue;
+    float* out = dq + (row * h + hh) * DQK + nb0 * 16 + 4 * g;
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb)
+      *reinterpret_cast<f32x4*>(out + nb * 16) = acc[hb][nb] * scale;
+  }
 }
 
 // ---------------------------------------------------------------- 3. dK, dV
