@@ -20,6 +20,8 @@
 // bitonic network held in registers (lane shuffles within a wave, LDS across waves) and
 // written out.  Rows with no more visible pools than k sort the whole prefix.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,43 +34,75 @@ constexpr int kMaxK = 4096;
 constexpr int kBins0 = 4096;  // first digit: the top 12 bits of the key
 constexpr int kCand = 4096;   // candidate list: keys of the first digit's threshold bin
 constexpr int kLoads = 2;     // float4 loads in flight per thread while streaming a row
-constexpr int kSampleMinVis = 32768;  // rows at least this long take the sampled select
-constexpr int kPeelMax = 8;           // winners peeled off before a halved final sort
+constexpr int kListF4 = 4;    // float4 per thread of a row read whole (list select)
+constexpr int kRefineBin = 512;  // expected row keys in a sample bin that call for a second round
+constexpr int kRankBuckets = 2048;    // buckets of the ranking sort of the winners
+constexpr int kRankMaxBucket = 64;    // a fuller bucket (heavy ties) takes the bitonic network
+constexpr int64_t kMarkedRowsGrid = 256;  // blocks of the pass over marked rows (1 per CU)
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t index) {
   return (static_cast<uint64_t>(~key) << 32) | index;  // ascending = key desc, index asc
 }
 
+// Order-preserving uint32 key of a score (larger score -> larger key, -0 as +0) in four
+// VALU operations: adding +0 turns -0 into +0 and leaves every other value as it is, then
+// negative values have all their bits flipped and the others their sign bit set.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+}
+
+// Inclusive scan of one uint32 per lane over the wave: DPP row shifts by 1, 2, 4 and 8 within
+// each row of 16 lanes (lanes without a source add 0), then the totals of the lower rows,
+// read from lanes 15, 31 and 47 into scalar registers.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xF, 0xF, false));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 15));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 31));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 47));
+  const int lane = threadIdx.x & 63;
+  x += lane >= 16 ? r0 : 0u;
+  x += lane >= 32 ? r1 : 0u;
+  x += lane >= 48 ? r2 : 0u;
+  return x;
+}
+
 // Block-wide exclusive scan of one uint32 per thread; returns the exclusive prefix and
-// writes the block total to *total.  All threads must call it.
+// writes the block total to *total.  All threads call it, and the block is synchronised
+// again before the next call (wave_tmp is rewritten).  One barrier: every wave reads all
+// the wave totals and adds those below its own.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tmp,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_inclusive_scan(v);
   if (lane == 63) wave_tmp[wid] = incl;
   __syncthreads();
-  if (wid == 0) {
-    uint32_t w = lane < kTopkWaves ? wave_tmp[lane] : 0u;
-    uint32_t wi = w;
+  uint32_t below = 0u, all = 0u;
 #pragma unroll
-    for (int off = 1; off < kTopkWaves; off <<= 1) {
-      const uint32_t o = __shfl_up(wi, off, 64);
-      if (lane >= off) wi += o;
-    }
-    if (lane < kTopkWaves) wave_tmp[kTopkWaves + lane] = wi - w;  // exclusive wave offsets
-    if (lane == kTopkWaves - 1) wave_tmp[2 * kTopkWaves] = wi;
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t t = wave_tmp[w];
+    below += w < wid ? t : 0u;
+    all += t;
   }
-  __syncthreads();
-  const uint32_t res = wave_tmp[kTopkWaves + wid] + incl - v;
-  *total = wave_tmp[2 * kTopkWaves];
-  __syncthreads();  // wave_tmp may be reused right after
-  return res;
+  *total = all;
+  return below + incl - v;
+}
+
+// Reserves for each lane cnt consecutive slots of a list whose length is the LDS counter
+// *len, with one atomic per wave, and returns the lane's first slot.  Every lane of the
+// wave calls it.
+__device__ __forceinline__ uint32_t wave_append(uint32_t cnt, uint32_t* len) {
+  const uint32_t incl = wave_inclusive_scan(cnt);
+  const uint32_t total =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  uint32_t base = 0u;
+  if (total != 0u && (threadIdx.x & 63) == 63) base = atomicAdd(len, total);
+  base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), 63));
+  return base + incl - cnt;
 }
 
 // Value of lane (lane ^ LS) of the wave, by VALU cross-lane moves: DPP quad permutes for 1
@@ -111,6 +145,30 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int ls) {
     case 16: return lane_xor_u64<16>(v);
     default: return lane_xor_u64<32>(v);
   }
+}
+
+// Wave-wide minimum and maximum of one uint32 per lane (a butterfly of VALU lane exchanges;
+// every lane gets the result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  uint32_t o;
+  o = lane_xor<1>(x); x = o < x ? o : x;
+  o = lane_xor<2>(x); x = o < x ? o : x;
+  o = lane_xor<4>(x); x = o < x ? o : x;
+  o = lane_xor<8>(x); x = o < x ? o : x;
+  o = lane_xor<16>(x); x = o < x ? o : x;
+  o = lane_xor<32>(x); x = o < x ? o : x;
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  uint32_t o;
+  o = lane_xor<1>(x); x = o > x ? o : x;
+  o = lane_xor<2>(x); x = o > x ? o : x;
+  o = lane_xor<4>(x); x = o > x ? o : x;
+  o = lane_xor<8>(x); x = o > x ? o : x;
+  o = lane_xor<16>(x); x = o > x ? o : x;
+  o = lane_xor<32>(x); x = o > x ? o : x;
+  return x;
 }
 
 // Ascending bitonic sort of buf[0, 1024 R).  Index bits [0, log2 R) select one of the R
@@ -184,24 +242,6 @@ __device__ __forceinline__ void sort_keys(uint64_t* buf, uint64_t* alt, int n2) 
     bitonic_sort_regs<4>(buf, alt);
 }
 
-// First digit window of a select over keys known to lie in [lo, hi]: they share the bits
-// above the highest bit where lo and hi differ (mask, prefix), and the 10-bit window ends at
-// that bit, so the keys spread over the histogram instead of piling into the few bins of a
-// shared exponent (fewer digit rounds and fewer colliding LDS atomics).
-__device__ __forceinline__ void digit_window(uint32_t lo, uint32_t hi, uint32_t* mask,
-                                             uint32_t* prefix, int* shift) {
-  const uint32_t diff = lo ^ hi;
-  if (diff == 0u) {  // one key value: a single window over the low bits, ties by pool
-    *mask = 0xFFFFFC00u;
-    *shift = 0;
-  } else {
-    const int hb = 31 - __builtin_clz(diff);
-    *mask = ~((2u << hb) - 1u);  // 2u << 31 == 0: no shared bits
-    *shift = hb >= 9 ? hb - 9 : 0;
-  }
-  *prefix = lo & *mask;
-}
-
 __device__ __forceinline__ int next_pow2(int n) {
   int p = 1;
   while (p < n) p <<= 1;
@@ -210,7 +250,8 @@ __device__ __forceinline__ int next_pow2(int n) {
 
 // Picks, from a histogram of nbins bins (nbins / 1024 consecutive bins per thread, counted
 // from the top), the bin holding the need-th largest key: returns it and writes the count
-// of keys in higher bins and in the bin.  All threads call it.
+// of keys in higher bins and in the bin.  All threads call it; the histogram may be
+// rewritten as soon as it returns.
 __device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, int nbins, uint32_t need,
                                              uint32_t* wave_tmp, uint32_t* pick,
                                              uint32_t* above_bin, uint32_t* in_bin) {
@@ -236,40 +277,59 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, int nbins, ui
   const uint32_t bin = pick[0];
   *above_bin = pick[1];
   *in_bin = pick[2];
-  __syncthreads();  // pick is rewritten by the next call
+  // The next call rewrites pick only after its scan's barrier, which every thread reaches
+  // after these reads; any other writer of pick synchronises the block first.
   return bin;
 }
 
-// FROM_CAND: the row's candidates come from a list written by the indexer (TopkCand)
-// instead of a score row; the row is flagged for the exact fallback when the list does not
-// hold between k and kCand entries.  Otherwise a non-null gate skips rows whose gate is 0.
-template <bool FROM_CAND>
-__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_kernel(const float* __restrict__ scores,
-                                                            int64_t ld, int64_t q_start,
-                                                            int64_t n_pools, int k,
-                                                            int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ gate,
-                                                            TopkCand cs) {
+// What one launch of topk_kernel does with its rows.
+enum TopkMode {
+  kTopkScoreRows = 0,  // score rows: the list paths, rows they cannot finish are marked
+  kTopkCandLists = 1,  // candidate lists written by the candidate-emitting indexer
+  kTopkMarkedRows = 2  // the exact two-pass select on the marked rows (persistent grid)
+};
+constexpr int32_t kRowMarked = -2;  // first output slot of a row left to the two-pass select
+
+// kTopkScoreRows: one block per row; a non-null gate skips rows whose gate is 0.  A row the
+// list paths cannot finish (the sampled list out of range: heavy ties or adversarial
+// layouts; k above the sampled path's limit) gets kRowMarked in its first output slot, and
+// the kTopkMarkedRows launch that follows on the same stream selects it exactly.
+// kTopkCandLists: the row's candidates come from a list written by the indexer (TopkCand);
+// the row is flagged for the exact fallback when the list does not hold between k and
+// kCand entries.
+template <int MODE>
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
+    MODE == kTopkMarkedRows ? 4 : 8, MODE == kTopkMarkedRows ? 4 : 8))) void topk_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t q_start, int64_t nq, int64_t n_pools,
+    int k, int32_t* __restrict__ idx, const int32_t* __restrict__ gate, TopkCand cs) {
   // The first-digit histogram is dead before the candidate list is written: they share LDS.
-  __shared__ uint64_t cand[kCand];  // (key << 32) | pool
+  __shared__ uint64_t cand[kCand];  // (key << 32) | pool; the ranking sort's grouped entries
   __shared__ uint32_t hist[1024];   // 10-bit digit histograms
-  __shared__ uint64_t buf[kMaxK];
+  __shared__ uint64_t buf[kMaxK];   // entries to sort: (~key << 32) | pool
   uint32_t* const hist0 = reinterpret_cast<uint32_t*>(cand);  // kBins0 counters
   static_assert(kBins0 * 4 <= kCand * 8, "first histogram fits the candidate list");
-  __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
+  __shared__ uint32_t wave_tmp[kTopkWaves];
   __shared__ uint32_t pick[3];
   __shared__ uint32_t fill[3];  // slots taken in buf and in cand; sample size
-  __shared__ uint32_t cand_max;  // largest key collected by the sampled path
-  __shared__ uint64_t peel_max[kTopkWaves];  // per-wave maxima while peeling the tail
-  __shared__ uint32_t peel_pos;
+  __shared__ uint32_t cand_max;  // largest key of a collected list
+  __shared__ uint32_t rbin[kRankBuckets + 1];  // ranking sort: bucket counts, then starts
+  __shared__ uint32_t rrange[3];  // ranking sort: smallest and largest ~key, fullest bucket
+  __shared__ uint32_t rcut;  // ranking sort: end of the bucket holding the last written position
+  __shared__ uint64_t marks[kTopkWaves];  // marked rows of a batch, one ballot per wave
 
   const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
-  if (!FROM_CAND && gate && gate[r] == 0) return;
-  const int64_t vis64 = visible_pools(q_start + r, n_pools);
-  const int vis = static_cast<int>(vis64);
-  const float* srow = scores + r * ld;
-  int32_t* orow = idx + r * k;
+  const int lane = tid & 63;
+  int64_t r = blockIdx.x;
+  int vis = 0, n4 = 0;
+  const float* srow = nullptr;
+  int32_t* orow = nullptr;
+  auto set_row = [&](int64_t row) {
+    r = row;
+    vis = static_cast<int>(visible_pools(q_start + row, n_pools));
+    n4 = (vis + 3) >> 2;  // float4 groups; the row is padded to ld (a multiple of 4)
+    srow = scores + row * ld;
+    orow = idx + row * k;
+  };
 
   // Exact resolution among the candidates cand[0, nc): the keys are known to hold every
   // key of the row that can still be selected above the current prefix (mask, prefix),
@@ -277,7 +337,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
   // window may overlap bits already fixed); a prefix held by more candidates than slots
   // after all 32 bits is an exact tie, resolved by pool.  Winners (keys above the prefix,
   // or on it and among the lowest pools) go to buf through fill[0].
-  auto resolve_candidates = [&](int nc, uint32_t prefix, uint32_t mask, int krem, int shift) {
+  auto resolve_candidates = [&](int nc, uint32_t prefix, uint32_t mask, int krem,
+                                int shift) __attribute__((always_inline)) {
     bool tied = false;
     uint32_t n_tied = 0u;  // candidates on the final prefix (when tied: the exact key)
     for (;; shift = shift > 10 ? shift - 10 : (shift > 0 ? 0 : -1)) {
@@ -355,53 +416,146 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     }
   };
 
-  // Sorts the k winners in buf[0, k) ascending on (~key, pool).  When k is a little above a
-  // power of two (k = 2051 of the Flash shape), the k - 2^m worst winners are peeled off to
-  // the tail first, largest first, by block-wide maxima (three barriers each), so the
-  // bitonic network sorts 2^m keys instead of 2^(m+1).
-  auto sort_winners = [&]() {
-    int n2 = max(next_pow2(k), kTopkThreads);
-    int kk = k;
-    const int half = n2 >> 1;
-    if (n2 > kTopkThreads && k - half <= kPeelMax) {
-      const int lane = tid & 63;
-      __syncthreads();  // every winner is in buf
-      for (int m = k; m > half; --m) {  // the largest of buf[0, m) goes to buf[m - 1]
-        uint64_t v = 0ull;
-        for (int j = tid; j < m; j += kTopkThreads) v = buf[j] > v ? buf[j] : v;
+  // Ranking sort of the n entries of buf[0, n) (distinct composites (~key << 32) | pool)
+  // into ascending order, i.e. score descending, lower pool first among equal scores.
+  // nlo <= nhi bound the entries' ~key.  Each entry goes to one of kRankBuckets buckets by a
+  // function of ~key that never decreases as ~key grows (a linear map of ~key - nlo in
+  // fp32, truncated), so every entry of a lower bucket sorts before every entry of a higher
+  // one; a block scan of the bucket counts gives each bucket's first position, and an
+  // entry's position is its bucket's start plus the number of entries of its bucket below
+  // it (exact 64-bit compares).  Scores near a selection threshold spread a few entries per
+  // bucket, so this costs a few LDS reads per entry instead of a sorting network's 66
+  // compare-exchange steps.  The pools of the first min(n, k) positions are left, in
+  // order, in the first words of buf.  Returns false, with buf untouched, when a bucket
+  // holds more than kRankMaxBucket entries (heavy ties).  rbin and rrange[2] are zero on
+  // entry; cand is free.
+  auto rank_sort = [&](int n, uint32_t nlo, uint32_t nhi) __attribute__((always_inline)) -> bool {
+    constexpr int kR = kMaxK / kTopkThreads;
+    uint32_t* const out32 = reinterpret_cast<uint32_t*>(buf);
+    uint64_t* const grp = cand;
+    const float inv = nhi > nlo ? static_cast<float>(kRankBuckets - 1) /
+                                      static_cast<float>(nhi - nlo)
+                                : 0.f;
+    auto bucket = [&](uint64_t x) {
+      const uint32_t nk = static_cast<uint32_t>(x >> 32);
+      const uint32_t b = static_cast<uint32_t>(static_cast<float>(nk - nlo) * inv);
+      return b < static_cast<uint32_t>(kRankBuckets - 1) ? b
+                                                         : static_cast<uint32_t>(kRankBuckets - 1);
+    };
+    const int nr = (n + kTopkThreads - 1) / kTopkThreads;  // uniform
+    uint32_t ds[kR];  // bucket << 16 | slot in the bucket
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const uint64_t o = lane_xor_u64(v, off);
-          v = o > v ? o : v;
-        }
-        if (lane == 0) peel_max[tid >> 6] = v;
-        __syncthreads();
-        uint64_t gm = peel_max[0];
-#pragma unroll
-        for (int w = 1; w < kTopkWaves; ++w) gm = peel_max[w] > gm ? peel_max[w] : gm;
-        for (int j = tid; j < m; j += kTopkThreads)
-          if (buf[j] == gm) peel_pos = static_cast<uint32_t>(j);  // winners are distinct
-        __syncthreads();
-        if (tid == 0) {
-          const uint32_t pos = peel_pos;
-          buf[pos] = buf[m - 1];
-          buf[m - 1] = gm;
-        }
-        __syncthreads();
+    for (int j = 0; j < kR; ++j) {
+      const int i = tid + j * kTopkThreads;
+      ds[j] = 0u;
+      if (j < nr && i < n) {
+        const uint32_t d = bucket(buf[i]);
+        ds[j] = (d << 16) | atomicAdd(&rbin[d], 1u);
       }
-      n2 = half;
-      kk = half;
     }
-    for (int i = kk + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
     __syncthreads();
-    sort_keys(buf, cand, n2);
+    // Bucket starts: two buckets per thread, one block scan; the fullest bucket's count.
+    static_assert(kRankBuckets == 2 * kTopkThreads, "two buckets per thread");
+    const uint32_t c0 = rbin[2 * tid], c1 = rbin[2 * tid + 1];
+    const uint32_t cmax = wave_max_u32(c0 > c1 ? c0 : c1);
+    if (lane == 0) atomicMax(&rrange[2], cmax);
+    uint32_t total;
+    const uint32_t start = block_exclusive_scan(c0 + c1, wave_tmp, &total);
+    rbin[2 * tid] = start;
+    rbin[2 * tid + 1] = start + c0;
+    if (tid == 0) rbin[kRankBuckets] = static_cast<uint32_t>(n);
+    // Only the first n_out positions are written out: entries of buckets that start at or
+    // past n_out are neither grouped nor ranked, and the grouped positions below `cut`, the
+    // end of the bucket holding position n_out - 1, are the ones ranked.
+    const uint32_t n_out = static_cast<uint32_t>(n < k ? n : k);
+    if (start < n_out && start + c0 >= n_out) rcut = start + c0;
+    if (start + c0 < n_out && start + c0 + c1 >= n_out) rcut = start + c0 + c1;
+    __syncthreads();
+    if (rrange[2] > static_cast<uint32_t>(kRankMaxBucket)) return false;  // uniform
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      const int i = tid + j * kTopkThreads;
+      if (j < nr && i < n) {
+        const uint32_t st = rbin[ds[j] >> 16];
+        if (st < n_out) grp[st + (ds[j] & 0xFFFFu)] = buf[i];
+      }
+    }
+    const int cut = static_cast<int>(rcut);
+    __syncthreads();
+    // Rank within the bucket; consecutive threads take consecutive grouped entries, so the
+    // lanes of a wave mostly scan the same bucket (broadcast LDS reads, even loop counts).
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      const int p = tid + j * kTopkThreads;
+      if (j < nr && p < cut) {
+        const uint64_t x = grp[p];
+        const uint32_t d = bucket(x);
+        const uint32_t s = rbin[d], c = rbin[d + 1] - s;
+        uint32_t rk = 0u;
+        for (uint32_t q = 0; q < c; ++q) rk += grp[s + q] < x ? 1u : 0u;
+        out32[s + rk] = static_cast<uint32_t>(x);
+      }
+    }
+    __syncthreads();
+    return true;
   };
 
-  if constexpr (FROM_CAND) {
+  // Writes the first min(k, n) of the n entries of buf[0, n) (n <= kMaxK) to the output row
+  // in sorted order, -1 in the slots past n.  nlo <= nhi bound the entries' ~key, or nlo >
+  // nhi to have them found here.  The ranking sort, or for heavy ties the bitonic network
+  // over buf padded with ~0 to a power of two.  All threads call it after writing buf.
+  auto sort_and_store = [&](int n, uint32_t nlo, uint32_t nhi) __attribute__((always_inline)) {
+    if (n == 0) {
+      for (int i = tid; i < k; i += kTopkThreads) orow[i] = -1;
+      return;
+    }
+    const bool find = nlo > nhi;
+    for (int b = tid; b <= kRankBuckets; b += kTopkThreads) rbin[b] = 0u;
+    if (tid == 0) {
+      rrange[2] = 0u;
+      if (find) {
+        rrange[0] = ~0u;
+        rrange[1] = 0u;
+      }
+    }
+    __syncthreads();  // buf written; rbin and rrange initialised
+    if (find) {
+      uint32_t lo = ~0u, hi = 0u;
+      for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t nk = static_cast<uint32_t>(buf[i] >> 32);
+        lo = nk < lo ? nk : lo;
+        hi = nk > hi ? nk : hi;
+      }
+      lo = wave_min_u32(lo);
+      hi = wave_max_u32(hi);
+      if (lane == 0 && lo <= hi) {
+        atomicMin(&rrange[0], lo);
+        atomicMax(&rrange[1], hi);
+      }
+      __syncthreads();
+      nlo = rrange[0];
+      nhi = rrange[1];
+    }
+    if (rank_sort(n, nlo, nhi)) {
+      const uint32_t* out32 = reinterpret_cast<const uint32_t*>(buf);
+      for (int i = tid; i < k; i += kTopkThreads)
+        orow[i] = i < n ? static_cast<int32_t>(out32[i]) : -1;
+      return;
+    }
+    const int n2 = max(next_pow2(n), kTopkThreads);
+    for (int i = n + tid; i < n2; i += kTopkThreads) buf[i] = ~0ull;
+    __syncthreads();
+    sort_keys(buf, cand, n2);
+    for (int i = tid; i < k; i += kTopkThreads)
+      orow[i] = i < n ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
+  };
+
+  if constexpr (MODE == kTopkCandLists) {
+    set_row(blockIdx.x);
     // The list holds every visible entry whose key is >= the row's threshold (all visible
     // entries when the threshold is 0).  With at least k (or all vis <= k) and at most kCand
-    // of them it holds the k winners, resolved here as in the sampled path; any other count
-    // leaves the row to the fallback (indexer scores + the score-row select).
+    // of them it holds the k winners: the whole list is sorted and its first k written.  Any
+    // other count leaves the row to the fallback (indexer scores + the score-row select).
     // Every list has room for kCand entries: all of it is requested before the count
     // arrives (entries past the count are ignored), so the loads take one round trip.
     static_assert(kCand == 4 * kTopkThreads, "four list entries per thread");
@@ -410,173 +564,244 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
 #pragma unroll
     for (int u = 0; u < 4; ++u) pre[u] = crow[u * kTopkThreads + tid];
     const uint32_t n = cs.cnt[r];
+    const uint32_t t_est = cs.t_est[r];
     const bool usable = vis <= k ? n == static_cast<uint32_t>(vis)
                                  : (n >= static_cast<uint32_t>(k) &&
                                     n <= static_cast<uint32_t>(kCand));
     if (tid == 0) {
       cs.fail[r] = usable ? 0 : 1;
       if (!usable) atomicOr(cs.any_fail, 1);
+      cand_max = 0u;
     }
     if (!usable) return;
-    if (vis <= k) {
-      const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = u * kTopkThreads + tid;
-        if (i < n2)
-          buf[i] = i < vis ? composite(static_cast<uint32_t>(pre[u] >> 32),
-                                       static_cast<uint32_t>(pre[u]))
-                           : ~0ull;
-      }
-      __syncthreads();
-      sort_keys(buf, cand, n2);
-      for (int i = tid; i < k; i += kTopkThreads)
-        orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
-      return;
-    }
-    if (tid < 3) fill[tid] = 0u;
-    if (tid == 0) cand_max = 0u;
-    __syncthreads();
+    __syncthreads();  // cand_max cleared
     uint32_t my_max = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = u * kTopkThreads + tid;
       if (i < static_cast<int>(n)) {
-        cand[i] = pre[u];
         const uint32_t key = static_cast<uint32_t>(pre[u] >> 32);
+        buf[i] = composite(key, static_cast<uint32_t>(pre[u]));
         my_max = key > my_max ? key : my_max;
       }
     }
-    if (my_max) atomicMax(&cand_max, my_max);
+    my_max = wave_max_u32(my_max);
+    if (lane == 0 && my_max) atomicMax(&cand_max, my_max);
     __syncthreads();
-    const uint32_t t_est = cs.t_est[r];
-    uint32_t mask, prefix;
-    int shift;
-    digit_window(t_est, cand_max, &mask, &prefix, &shift);
-    resolve_candidates(static_cast<int>(n), prefix, mask, k, shift);
-    sort_winners();
-    for (int i = tid; i < k; i += kTopkThreads)
-      orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
+    // Keys lie in [t_est, cand_max]; a zero threshold gives no useful bound.
+    if (t_est == 0u)
+      sort_and_store(static_cast<int>(n), 1u, 0u);
+    else
+      sort_and_store(static_cast<int>(n), ~cand_max, ~t_est);
     return;
   }
 
-  if (vis <= k) {
-    const int n2 = max(next_pow2(vis > 0 ? vis : 1), kTopkThreads);
-    for (int i = tid; i < n2; i += kTopkThreads)
-      buf[i] = i < vis ? composite(float_order_key(srow[i]), static_cast<uint32_t>(i)) : ~0ull;
-    __syncthreads();
-    sort_keys(buf, cand, n2);
-    for (int i = tid; i < k; i += kTopkThreads)
-      orow[i] = i < vis ? static_cast<int32_t>(buf[i] & 0xFFFFFFFFu) : -1;
-    return;
-  }
-
-  const int n4 = (vis + 3) >> 2;  // float4 groups; the row is padded to ld (a multiple of 4)
   // Calls f(i4, v) for every float4 group of the row, kLoads loads in flight per thread.
   // Groups past the row end carry keys with index >= vis, which f must skip.
-  auto stream_row = [&](auto&& f) {
-    for (int base = 0; base < n4; base += kLoads * kTopkThreads) {
-      f32x4 v[kLoads];
+  auto stream_row_with = [&](auto loads, auto&& f) {
+    constexpr int kNL = decltype(loads)::value;
+    for (int base = 0; base < n4; base += kNL * kTopkThreads) {
+      f32x4 v[kNL];
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
+      for (int u = 0; u < kNL; ++u) {
         const int i4 = base + u * kTopkThreads + tid;
         v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) f(base + u * kTopkThreads + tid, v[u]);
+      for (int u = 0; u < kNL; ++u) f(base + u * kTopkThreads + tid, v[u]);
+    }
+  };
+  auto stream_row = [&](auto&& f) {
+    stream_row_with(std::integral_constant<int, kLoads>(), f);
+  };
+
+  // Rows longer than kCand.  Rows of up to kListVis pools are read whole into registers
+  // (kListF4 float4 per thread); longer rows read a 1/16 sample (256-byte pieces, one every
+  // 4 KB of the row, or sparser past 2^18 keys: at most 256 pieces, four per group of 16
+  // threads).  A 12-bit histogram of those keys, its window starting at the highest bit
+  // where their smallest and largest keys differ (so they spread over the bins instead of
+  // piling into the few bins of a shared exponent), picks the bin holding the k-th largest
+  // key of a whole row, or for a sample the key ranked 1.5 k scaled to the sample.  A whole
+  // row then lists, from registers, every key in that bin or above it (k plus the bin's
+  // few keys); a sampled row is streamed once more and every key at or above the bin's
+  // lower edge listed (about 1.5 k).  The list (at most kMaxK entries, and at least k for a
+  // sampled row) holds the k winners and is sorted whole, its first k written.  Any other
+  // list size (heavy ties, layouts that fool the sample) returns false.
+  auto list_select = [&](auto whole_c) __attribute__((always_inline)) -> bool {
+    constexpr bool kWhole = decltype(whole_c)::value;
+    const int piece_stride = 256 * ((n4 + 65535) / 65536);
+    // Rounds of groups held: a whole row nu rounds of 1024 float4, a sample nu rounds of 64
+    // pieces.  Slots past the row hold key 0, below the key of every score.
+    int nu = 0;
+    if constexpr (kWhole) {
+      nu = (n4 + kTopkThreads - 1) / kTopkThreads;
+    } else {
+      while (nu < kListF4 && piece_stride * 64 * nu < n4) ++nu;
+    }
+    auto index4 = [&](int u) {  // float4 group of round u
+      if constexpr (kWhole) return u * kTopkThreads + tid;
+      else return piece_stride * ((tid >> 4) + 64 * u) + (tid & 15);
+    };
+    f32x4 x[kListF4];
+#pragma unroll
+    for (int u = 0; u < kListF4; ++u) {
+      const int i4 = index4(u);
+      x[u] = u < nu && i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
+    if (tid == 0) {
+      fill[0] = 0u;
+      fill[1] = 0u;
+      fill[2] = 0u;
+      cand_max = 0u;
+      rrange[0] = ~0u;
+      rrange[1] = 0u;
+    }
+    uint32_t key[4 * kListF4];
+    uint32_t lo1 = ~0u, hi = 0u, n_local = 0u;  // lo1: smallest key - 1 (key 0 is neutral)
+#pragma unroll
+    for (int u = 0; u < kListF4; ++u) {
+      if (u < nu) {  // uniform
+        const int nv = min(max(vis - 4 * index4(u), 0), 4);
+        n_local += static_cast<uint32_t>(nv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[4 * u + e] = e < nv ? score_key(x[u][e]) : 0u;
+          lo1 = min(lo1, key[4 * u + e] - 1u);
+          hi = max(hi, key[4 * u + e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * u + e] = 0u;
+      }
+    }
+    lo1 = wave_min_u32(lo1);
+    hi = wave_max_u32(hi);
+    __syncthreads();  // histogram, counters and range cleared
+    if (lane == 0) {
+      atomicMin(&rrange[0], lo1);
+      atomicMax(&rrange[1], hi);
+    }
+    if (!kWhole && n_local) atomicAdd(&fill[2], n_local);
+    __syncthreads();
+    const uint32_t klo = rrange[0] + 1u, khi = rrange[1];
+    const uint32_t n_keys = kWhole ? static_cast<uint32_t>(vis) : fill[2];
+    const uint32_t diff = klo ^ khi;
+    const int hb = diff != 0u ? 31 - __builtin_clz(diff) : 0;
+    const int shift = hb >= 11 ? hb - 11 : 0;
+#pragma unroll
+    for (int u = 0; u < kListF4; ++u)
+      if (u < nu)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key[4 * u + e] != 0u) atomicAdd(&hist0[(key[4 * u + e] >> shift) & 0xFFFu], 1u);
+    __syncthreads();
+    uint32_t rank = static_cast<uint32_t>(k);
+    if constexpr (!kWhole) {
+      const int64_t target = k + k / 2;
+      rank = static_cast<uint32_t>((target * n_keys + vis / 2) / vis);
+      rank = rank < 1u ? 1u : (rank > n_keys ? n_keys : rank);
+    }
+    uint32_t above0, in0;
+    const uint32_t b0 = pick_bin(hist0, kBins0, rank, wave_tmp, pick, &above0, &in0);
+    // Lower edge of bin b0: the bits above the window as in the largest key, the window b0.
+    uint32_t lower = (khi & ~((0x1000u << shift) - 1u)) | (b0 << shift);
+    if constexpr (kWhole) {
+      const uint32_t n = above0 + in0;
+      if (n > static_cast<uint32_t>(kMaxK)) return false;  // uniform
+      // Key 0 (no score) never reaches a bin edge.
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int u = 0; u < kListF4; ++u)
+        if (u < nu)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cnt += key[4 * u + e] >= lower ? 1u : 0u;
+      uint32_t slot = wave_append(cnt, &fill[0]);
+#pragma unroll
+      for (int u = 0; u < kListF4; ++u)
+        if (u < nu)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (key[4 * u + e] >= lower) {
+              if (slot < static_cast<uint32_t>(kMaxK))
+                buf[slot] = composite(key[4 * u + e], static_cast<uint32_t>(4 * index4(u) + e));
+              ++slot;
+            }
+      sort_and_store(static_cast<int>(n), ~khi, ~lower);
+      return true;
+    } else {
+      // A sample bin expected to hold many of the row's keys (a window spanning several
+      // exponents): a second 12-bit round over the sample keys inside it.
+      if (shift > 0 && static_cast<uint64_t>(in0) * static_cast<uint64_t>(vis) >
+                           static_cast<uint64_t>(kRefineBin) * n_keys) {
+        const int shift2 = shift >= 12 ? shift - 12 : 0;
+        const uint32_t fixed = ~((1u << shift) - 1u);
+        for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kListF4; ++u)
+          if (u < nu)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if ((key[4 * u + e] & fixed) == lower)
+                atomicAdd(&hist0[(key[4 * u + e] >> shift2) & 0xFFFu], 1u);
+        __syncthreads();
+        uint32_t above1, in1;
+        const uint32_t b1 = pick_bin(hist0, kBins0, rank - above0, wave_tmp, pick, &above1, &in1);
+        lower = (lower & ~(0xFFFu << shift2)) | (b1 << shift2);
+      }
+      // One pass over the row: every key at or above lower is listed, kListF4 float4 per
+      // thread in flight, one list reservation per wave and pass.
+      uint32_t my_max = 0u;
+      for (int base = 0; base < n4; base += kListF4 * kTopkThreads) {
+        f32x4 v[kListF4];
+#pragma unroll
+        for (int u = 0; u < kListF4; ++u) {
+          const int i4 = base + u * kTopkThreads + tid;
+          v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int u = 0; u < kListF4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * (base + u * kTopkThreads + tid) + e;
+            const uint32_t kk = score_key(v[u][e]);
+            const bool take = i < vis && kk >= lower;
+            cnt += take ? 1u : 0u;
+            my_max = take ? max(my_max, kk) : my_max;
+          }
+        uint32_t slot = wave_append(cnt, &fill[1]);
+#pragma unroll
+        for (int u = 0; u < kListF4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * (base + u * kTopkThreads + tid) + e;
+            const uint32_t kk = score_key(v[u][e]);
+            if (i < vis && kk >= lower) {
+              if (slot < static_cast<uint32_t>(kCand))
+                buf[slot] = composite(kk, static_cast<uint32_t>(i));
+              ++slot;
+            }
+          }
+      }
+      my_max = wave_max_u32(my_max);
+      if (lane == 0 && my_max) atomicMax(&cand_max, my_max);
+      __syncthreads();
+      const uint32_t n_cand = fill[1];
+      if (n_cand < static_cast<uint32_t>(k) || n_cand > static_cast<uint32_t>(kCand))
+        return false;
+      // The listed keys lie in [lower, cand_max].
+      sort_and_store(static_cast<int>(n_cand), ~cand_max, ~lower);
+      return true;
     }
   };
 
-  // Long rows: estimate the key ranked about 1.5 k from a 1/16 sample of the row, then
-  // one pass collects every key at or above the estimate into the candidate list.  When
-  // the list holds at least k and at most kCand keys it contains the k winners, which are
-  // then resolved from LDS alone: the row is read 1 1/16 times instead of twice.  Any
-  // other count (rare; heavy ties) falls back to the two-pass select below.
-  bool sampled = false;
-  if (vis >= kSampleMinVis && 3 * k <= 2 * kCand) {
-    if (tid < 3) fill[tid] = 0u;
-    if (tid == 0) cand_max = 0u;
-    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-    __syncthreads();
-    // The sample: 256-byte pieces (16 float4), one every 4 KB (256 float4) of the row, or
-    // sparser on rows past 2^18 keys so that there are at most 256 pieces: four per group
-    // of 16 threads, all loaded before any is used (one memory latency per sample pass).
-    const int piece_stride = 256 * ((n4 + 65535) / 65536);
-    auto stream_sample = [&](auto&& f) {
-      f32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i4 = piece_stride * ((tid >> 4) + 64 * j) + (tid & 15);
-        v[j] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f(piece_stride * ((tid >> 4) + 64 * j) + (tid & 15), v[j]);
-    };
-    uint32_t n_local = 0u;
-    stream_sample([&](int i4, const f32x4& v) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * i4 + e < vis) {
-          atomicAdd(&hist[float_order_key(v[e]) >> 22], 1u);
-          ++n_local;
-        }
-    });
-    if (n_local) atomicAdd(&fill[2], n_local);
-    __syncthreads();
-    const uint32_t n_sample = fill[2];
-    // Rank of the estimate in the sample: 1.5 k scaled to the sample (at least 1).
-    const int64_t target = k + k / 2;
-    uint32_t rank = static_cast<uint32_t>((target * n_sample + vis / 2) / vis);
-    rank = rank < 1u ? 1u : (rank > n_sample ? n_sample : rank);
-    uint32_t above1, in1;
-    const uint32_t bin1 = pick_bin(hist, 1024, rank, wave_tmp, pick, &above1, &in1);
-    const uint32_t prefix1 = bin1 << 22;
-    for (int b = tid; b < 1024; b += kTopkThreads) hist[b] = 0u;
-    __syncthreads();
-    stream_sample([&](int i4, const f32x4& v) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = float_order_key(v[e]);
-        if (4 * i4 + e < vis && (key & 0xFFC00000u) == prefix1)
-          atomicAdd(&hist[(key >> 12) & 0x3FFu], 1u);
-      }
-    });
-    __syncthreads();
-    uint32_t above2, in2;
-    const uint32_t bin2 = pick_bin(hist, 1024, rank - above1, wave_tmp, pick, &above2, &in2);
-    const uint32_t t_est = prefix1 | (bin2 << 12);  // lower edge of the estimate's 20-bit bin
-    uint32_t my_max = 0u;
-    stream_row([&](int i4, const f32x4& v) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
-        const uint32_t key = float_order_key(v[e]);
-        if (static_cast<int>(i) < vis && key >= t_est) {
-          const uint32_t slot = atomicAdd(&fill[1], 1u);
-          if (slot < static_cast<uint32_t>(kCand))
-            cand[slot] = (static_cast<uint64_t>(key) << 32) | i;
-          my_max = key > my_max ? key : my_max;
-        }
-      }
-    });
-    if (my_max) atomicMax(&cand_max, my_max);
-    __syncthreads();
-    const uint32_t n_cand = fill[1];
-    sampled = n_cand >= static_cast<uint32_t>(k) && n_cand <= static_cast<uint32_t>(kCand);
-    __syncthreads();  // fill[] is reset below
-    if (sampled) {
-      // The candidates lie in [t_est, cand_max]: the top bits those two share are fixed, and
-      // the select starts right below them.
-      uint32_t mask, prefix;
-      int shift;
-      digit_window(t_est, cand_max, &mask, &prefix, &shift);
-      resolve_candidates(static_cast<int>(n_cand), prefix, mask, k, shift);
-    }
-  }
-
-  if (!sampled) {
+  // The exact two-pass select; the k winners end in buf.
+  auto two_pass_select = [&]() __attribute__((always_inline)) {
     // Pass A: the top 12 bits of every visible key.
     for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
     if (tid < 2) fill[tid] = 0u;
@@ -584,7 +809,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
     stream_row([&](int i4, const f32x4& v) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * i4 + e < vis) atomicAdd(&hist0[float_order_key(v[e]) >> 20], 1u);
+        if (4 * i4 + e < vis) atomicAdd(&hist0[score_key(v[e]) >> 20], 1u);
     });
     __syncthreads();
     uint32_t above0, in0;
@@ -602,7 +827,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t i = static_cast<uint32_t>(4 * i4 + e);
-          const uint32_t key = float_order_key(v[e]);
+          const uint32_t key = score_key(v[e]);
           const uint32_t d = key >> 20;
           if (static_cast<int>(i) < vis && d >= b0) {
             if (d > b0 || whole)
@@ -625,7 +850,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
         stream_row([&](int i4, const f32x4& v) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t key = float_order_key(v[e]);
+            const uint32_t key = score_key(v[e]);
             if (4 * i4 + e < vis && (key & mask) == prefix)
               atomicAdd(&hist[(key >> shift) & 0x3FFu], 1u);
           }
@@ -657,7 +882,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
 #pragma unroll
         for (int e = 0; e < 4 * kU; ++e) {
           const int i = 4 * (base4 + kU * tid) + e;
-          const uint32_t mk = float_order_key(cur[e >> 2][e & 3]) & mask;
+          const uint32_t mk = score_key(cur[e >> 2][e & 3]) & mask;
           if (i < vis) {
             if (mk > prefix) {
               flags |= 1u << e;
@@ -670,13 +895,14 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
         }
         uint32_t tot;
         const uint32_t pre = block_exclusive_scan(cgt | (ceq << 16), wave_tmp, &tot);
+        __syncthreads();  // wave_tmp is rewritten by the next group's scan
         if (flags != 0u) {
           uint32_t pos_gt = run_gt + (pre & 0xFFFFu);
           uint32_t rank_eq = run_eq + (pre >> 16);
 #pragma unroll
           for (int e = 0; e < 4 * kU; ++e) {
             const uint32_t i = static_cast<uint32_t>(4 * (base4 + kU * tid) + e);
-            const uint32_t key = float_order_key(cur[e >> 2][e & 3]);
+            const uint32_t key = score_key(cur[e >> 2][e & 3]);
             if (flags & (1u << e)) {
               buf[pos_gt++] = composite(key, i);
             } else if (flags & (1u << (16 + e))) {
@@ -690,11 +916,50 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8,
         if (run_gt >= n_gt && run_eq >= static_cast<uint32_t>(krem)) break;  // uniform
       }
     }
-  }
+  };
 
-  sort_winners();
-  for (int i = tid; i < k; i += kTopkThreads)
-    orow[i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFu);
+  if constexpr (MODE == kTopkScoreRows) {
+    if (gate && gate[blockIdx.x] == 0) return;
+    set_row(blockIdx.x);
+    if (vis <= kCand) {
+      // Every visible key fits the list (rows with at most k visible pools included): the
+      // row is sorted whole and its first k entries written.
+      for (int i = tid; i < vis; i += kTopkThreads)
+        buf[i] = composite(score_key(srow[i]), static_cast<uint32_t>(i));
+      sort_and_store(vis, 1u, 0u);
+      return;
+    }
+    if (3 * k <= 2 * kCand) {
+      const bool done = n4 <= kListF4 * kTopkThreads ? list_select(std::true_type())
+                                                     : list_select(std::false_type());
+      if (done) return;
+    }
+    if (tid == 0) orow[0] = kRowMarked;
+  } else if constexpr (MODE == kTopkMarkedRows) {
+    // Block b looks at rows b, b + G, b + 2 G, ... (G blocks), 1024 of them per batch: one
+    // load of each row's first slot, the marked ones collected as wave ballots, then each
+    // selected in turn by the whole block.
+    const int64_t g = gridDim.x;
+    for (int64_t base = blockIdx.x; base < nq; base += g * kTopkThreads) {
+      const int64_t row = base + static_cast<int64_t>(tid) * g;
+      const bool marked =
+          row < nq && (gate == nullptr || gate[row] != 0) && idx[row * k] == kRowMarked;
+      const uint64_t m = __ballot(marked);
+      if (lane == 0) marks[tid >> 6] = m;
+      __syncthreads();
+      for (int w = 0; w < kTopkWaves; ++w) {
+        uint64_t mm = marks[w];
+        while (mm != 0ull) {  // uniform
+          const int b = __builtin_ctzll(mm);
+          mm &= mm - 1ull;
+          set_row(base + static_cast<int64_t>(w * 64 + b) * g);
+          two_pass_select();
+          sort_and_store(k, 1u, 0u);
+        }
+      }
+      __syncthreads();  // marks is rewritten by the next batch
+    }
+  }
 }
 
 // Per-row threshold for the fused select, from the scores of every 2^shift-th visible pool
@@ -743,7 +1008,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool ok = 4 * i4 + e < vs;
-        const uint32_t kk = float_order_key(v[e]);
+        const uint32_t kk = score_key(v[e]);
         key[4 * u + e] = kk;
         kmax = ok && kk > kmax ? kk : kmax;
         kmin = ok && kk < kmin ? kk : kmin;
@@ -823,7 +1088,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(
         const int i4 = base + u * kTopkThreads + tid;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (4 * i4 + e < vs) f(float_order_key(v[u][e]));
+          if (4 * i4 + e < vs) f(score_key(v[u][e]));
       }
     }
   };
@@ -857,8 +1122,16 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t q_start, int64_t
                        hipStream_t stream, const int32_t* gate) {
   if (nq <= 0) return hipSuccess;
   if (nq >= (int64_t{1} << 31)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(topk_kernel<false>, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
-                     stream, scores, ld, q_start, n_pools, k, idx, gate, TopkCand());
+  hipLaunchKernelGGL(topk_kernel<kTopkScoreRows>, dim3(static_cast<unsigned>(nq)),
+                     dim3(kTopkThreads), 0, stream, scores, ld, q_start, nq, n_pools, k, idx,
+                     gate, TopkCand());
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Rows marked by the launch above (rare), one block per compute unit of the chip.
+  const int64_t grid = nq < kMarkedRowsGrid ? nq : kMarkedRowsGrid;
+  hipLaunchKernelGGL(topk_kernel<kTopkMarkedRows>, dim3(static_cast<unsigned>(grid)),
+                     dim3(kTopkThreads), 0, stream, scores, ld, q_start, nq, n_pools, k, idx,
+                     gate, TopkCand());
   return hipGetLastError();
 }
 
@@ -877,8 +1150,9 @@ hipError_t launch_topk_from_cand(const TopkCand& cs, int64_t q_start, int64_t nq
   if (nq <= 0) return hipSuccess;
   if (nq >= (int64_t{1} << 31) || cs.cap < kCand || !topk_fused_supported(k))
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(topk_kernel<true>, dim3(static_cast<unsigned>(nq)), dim3(kTopkThreads), 0,
-                     stream, nullptr, int64_t{0}, q_start, n_pools, k, idx, nullptr, cs);
+  hipLaunchKernelGGL(topk_kernel<kTopkCandLists>, dim3(static_cast<unsigned>(nq)),
+                     dim3(kTopkThreads), 0, stream, nullptr, int64_t{0}, q_start, nq, n_pools, k,
+                     idx, nullptr, cs);
   return hipGetLastError();
 }
 

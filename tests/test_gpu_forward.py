@@ -247,6 +247,29 @@ def test_topk_long_rows_sample_fallbacks(gpu, kind):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+def test_topk_many_marked_rows(gpu):
+    """Rows the list paths cannot finish are selected by a pass over marked rows with one
+    block per compute unit, each taking every G-th row in batches of 1024.  263144 rows of
+    4200 visible pools (more than 256 x 1024, so blocks run several batches and several rows
+    per batch): every third row all zero (the sampled list overflows: marked; ties go to the
+    lowest pools), the others distinct values (sampled list in range).  Both expected
+    results are closed forms: pools 0 .. k-1, and the pools of the k largest values."""
+    nq, p, k = 263144, 4200, 2048
+    say("case: topk %d rows, every third one marked" % nq)
+    pos = torch.arange(p, device=gpu, dtype=torch.int64)
+    distinct = ((pos * 7919) % p).to(torch.float32)
+    scores = distinct.repeat(nq, 1)
+    scores[0::3] = 0.0
+    idx = B.topk_new(scores, q_start=4 * p, n_pools=p, k=k)
+    torch.cuda.synchronize()
+    want_ties = torch.arange(k, device=gpu, dtype=torch.int32)
+    want_distinct = torch.argsort(distinct, descending=True)[:k].to(torch.int32)
+    assert bool((idx[0::3] == want_ties).all())
+    other = torch.ones(nq, dtype=torch.bool, device=gpu)
+    other[0::3] = False
+    assert bool((idx[other] == want_distinct).all())
+
+
 def test_topk_chunk_of_consecutive_rows(gpu):
     say("case: topk consecutive rows, clustered ints, q_start=100000")
     rng = np.random.default_rng(5)
