@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
   // order, in the first words of buf.  Returns false, with buf untouched, when a bucket
   // holds more than kRankMaxBucket entries (heavy ties).  rbin and rrange[2] are zero on
   // entry; cand is free.
-  auto rank_sort = [&](int n, uint32_t nlo, uint32_t nhi) __attribute__((always_inline)) -> bool {
+  auto rank_sort = [&](int n, uint32_t nlo, uint32_t nhi, bool raw) __attribute__((always_inline)) -> bool {
     constexpr int kR = kMaxK / kTopkThreads;
     uint32_t* const out32 = reinterpret_cast<uint32_t*>(buf);
     uint64_t* const grp = cand;
@@ -449,7 +449,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       const int i = tid + j * kTopkThreads;
       ds[j] = 0u;
       if (j < nr && i < n) {
-        const uint32_t d = bucket(buf[i]);
+        uint64_t x = buf[i];
+        if (raw) {  // (score bits << 32) | pool -> composite, written back
+          x = composite(score_key(__uint_as_float(static_cast<uint32_t>(x >> 32))),
+                        static_cast<uint32_t>(x));
+          buf[i] = x;
+        }
+        const uint32_t d = bucket(x);
         ds[j] = (d << 16) | atomicAdd(&rbin[d], 1u);
       }
     }
@@ -504,7 +510,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
   // in sorted order, -1 in the slots past n.  nlo <= nhi bound the entries' ~key, or nlo >
   // nhi to have them found here.  The ranking sort, or for heavy ties the bitonic network
   // over buf padded with ~0 to a power of two.  All threads call it after writing buf.
-  auto sort_and_store = [&](int n, uint32_t nlo, uint32_t nhi) __attribute__((always_inline)) {
+  auto sort_and_store = [&](int n, uint32_t nlo, uint32_t nhi, bool raw = false)
+                            __attribute__((always_inline)) {
     if (n == 0) {
       for (int i = tid; i < k; i += kTopkThreads) orow[i] = -1;
       return;
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       nlo = rrange[0];
       nhi = rrange[1];
     }
-    if (rank_sort(n, nlo, nhi)) {
+    if (rank_sort(n, nlo, nhi, raw)) {
       const uint32_t* out32 = reinterpret_cast<const uint32_t*>(buf);
       for (int i = tid; i < k; i += kTopkThreads)
         orow[i] = i < n ? static_cast<int32_t>(out32[i]) : -1;
@@ -699,9 +706,10 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
           if (key[4 * u + e] != 0u) atomicAdd(&hist0[(key[4 * u + e] >> shift) & 0xFFFu], 1u);
     __syncthreads();
     uint32_t rank = static_cast<uint32_t>(k);
-    if constexpr (!kWhole) {
-      const int64_t target = k + k / 2;
-      rank = static_cast<uint32_t>((target * n_keys + vis / 2) / vis);
+    if constexpr (!kWhole) {  // 1.5 k scaled to the sample (an estimate: fp32 will do)
+      rank = static_cast<uint32_t>(static_cast<float>(k + k / 2) * static_cast<float>(n_keys) /
+                                       static_cast<float>(vis) +
+                                   0.5f);
       rank = rank < 1u ? 1u : (rank > n_keys ? n_keys : rank);
     }
     uint32_t above0, in0;
@@ -752,9 +760,14 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
         const uint32_t b1 = pick_bin(hist0, kBins0, rank - above0, wave_tmp, pick, &above1, &in1);
         lower = (lower & ~(0xFFFu << shift2)) | (b1 << shift2);
       }
-      // One pass over the row: every key at or above lower is listed, kListF4 float4 per
-      // thread in flight, one list reservation per wave and pass.
-      uint32_t my_max = 0u;
+      // One pass over the row: every score whose key is at or above lower is listed as
+      // (score bits << 32) | pool, kListF4 float4 per thread in flight, one list reservation
+      // per wave and pass.  Scores are compared as floats against the smallest float of key
+      // lower (-inf when lower is below the key of -inf).
+      const float f_lower =
+          lower <= 0x007FFFFFu ? -__builtin_inff()
+                               : __uint_as_float((lower & 0x80000000u) ? lower ^ 0x80000000u : ~lower);
+      float my_max = -__builtin_inff();  // largest listed score
       for (int base = 0; base < n4; base += kListF4 * kTopkThreads) {
         f32x4 v[kListF4];
 #pragma unroll
@@ -765,37 +778,40 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
         }
         uint32_t cnt = 0u;
 #pragma unroll
-        for (int u = 0; u < kListF4; ++u)
+        for (int u = 0; u < kListF4; ++u) {
+          if (base + u * kTopkThreads < n4) {  // uniform
+            const int nv = min(max(vis - 4 * (base + u * kTopkThreads + tid), 0), 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * (base + u * kTopkThreads + tid) + e;
-            const uint32_t kk = score_key(v[u][e]);
-            const bool take = i < vis && kk >= lower;
-            cnt += take ? 1u : 0u;
-            my_max = take ? max(my_max, kk) : my_max;
+            for (int e = 0; e < 4; ++e) cnt += e < nv && v[u][e] >= f_lower ? 1u : 0u;
           }
+        }
         uint32_t slot = wave_append(cnt, &fill[1]);
 #pragma unroll
-        for (int u = 0; u < kListF4; ++u)
+        for (int u = 0; u < kListF4; ++u) {
+          if (base + u * kTopkThreads < n4) {  // uniform
+            const int i4 = base + u * kTopkThreads + tid;
+            const int nv = min(max(vis - 4 * i4, 0), 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * (base + u * kTopkThreads + tid) + e;
-            const uint32_t kk = score_key(v[u][e]);
-            if (i < vis && kk >= lower) {
-              if (slot < static_cast<uint32_t>(kCand))
-                buf[slot] = composite(kk, static_cast<uint32_t>(i));
-              ++slot;
-            }
+            for (int e = 0; e < 4; ++e)
+              if (e < nv && v[u][e] >= f_lower) {
+                if (slot < static_cast<uint32_t>(kCand))
+                  buf[slot] = (static_cast<uint64_t>(__float_as_uint(v[u][e])) << 32) |
+                              static_cast<uint32_t>(4 * i4 + e);
+                ++slot;
+                my_max = fmaxf(my_max, v[u][e]);
+              }
           }
+        }
       }
-      my_max = wave_max_u32(my_max);
-      if (lane == 0 && my_max) atomicMax(&cand_max, my_max);
+      // Keys of listed scores are >= lower > 0; a thread that listed none contributes 0.
+      const uint32_t max_key = wave_max_u32(my_max >= f_lower ? score_key(my_max) : 0u);
+      if (lane == 0 && max_key) atomicMax(&cand_max, max_key);
       __syncthreads();
       const uint32_t n_cand = fill[1];
       if (n_cand < static_cast<uint32_t>(k) || n_cand > static_cast<uint32_t>(kCand))
         return false;
-      // The listed keys lie in [lower, cand_max].
-      sort_and_store(static_cast<int>(n_cand), ~cand_max, ~lower);
+      // The listed keys lie in [lower, cand_max]; the entries hold raw scores.
+      sort_and_store(static_cast<int>(n_cand), ~cand_max, ~lower, true);
       return true;
     }
   };
