@@ -72,8 +72,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 
 // Block-wide exclusive scan of one uint32 per thread; returns the exclusive prefix and
 // writes the block total to *total.  All threads call it, and the block is synchronised
-// again before the next call (wave_tmp is rewritten).  One barrier: every wave reads all
-// the wave totals and adds those below its own.
+// again before the next call (wave_tmp is rewritten).  Each wave scans its own values; wave
+// 0 then scans the wave totals (wave_tmp holds 2 * kTopkWaves + 1 words).
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tmp,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63;
@@ -81,15 +81,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   const uint32_t incl = wave_inclusive_scan(v);
   if (lane == 63) wave_tmp[wid] = incl;
   __syncthreads();
-  uint32_t below = 0u, all = 0u;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t t = wave_tmp[w];
-    below += w < wid ? t : 0u;
-    all += t;
+  if (wid == 0) {
+    const uint32_t t = lane < kTopkWaves ? wave_tmp[lane] : 0u;
+    const uint32_t ti = wave_inclusive_scan(t);
+    if (lane < kTopkWaves) wave_tmp[kTopkWaves + lane] = ti - t;  // exclusive wave offsets
+    if (lane == kTopkWaves - 1) wave_tmp[2 * kTopkWaves] = ti;
   }
-  *total = all;
-  return below + incl - v;
+  __syncthreads();
+  *total = wave_tmp[2 * kTopkWaves];
+  return wave_tmp[kTopkWaves + wid] + incl - v;
 }
 
 // Reserves for each lane cnt consecutive slots of a list whose length is the LDS counter
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
   __shared__ uint64_t buf[kMaxK];   // entries to sort: (~key << 32) | pool
   uint32_t* const hist0 = reinterpret_cast<uint32_t*>(cand);  // kBins0 counters
   static_assert(kBins0 * 4 <= kCand * 8, "first histogram fits the candidate list");
-  __shared__ uint32_t wave_tmp[kTopkWaves];
+  __shared__ uint32_t wave_tmp[2 * kTopkWaves + 1];
   __shared__ uint32_t pick[3];
   __shared__ uint32_t fill[3];  // slots taken in buf and in cand; sample size
   __shared__ uint32_t cand_max;  // largest key of a collected list
@@ -650,13 +650,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       if constexpr (kWhole) return u * kTopkThreads + tid;
       else return piece_stride * ((tid >> 4) + 64 * u) + (tid & 15);
     };
+    // Groups past the row are read at the row's last group (the values are not used), so
+    // the loads need no branch.
     f32x4 x[kListF4];
 #pragma unroll
-    for (int u = 0; u < kListF4; ++u) {
-      const int i4 = index4(u);
-      x[u] = u < nu && i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int u = 0; u < kListF4; ++u)
+      if (u < nu)  // uniform
+        x[u] = *reinterpret_cast<const f32x4*>(srow + 4 * min(index4(u), n4 - 1));
     for (int b = tid; b < kBins0; b += kTopkThreads) hist0[b] = 0u;
     if (tid == 0) {
       fill[0] = 0u;
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
                   buf[slot] = (static_cast<uint64_t>(__float_as_uint(v[u][e])) << 32) |
                               static_cast<uint32_t>(4 * i4 + e);
                 ++slot;
-                my_max = fmaxf(my_max, v[u][e]);
+                my_max = v[u][e] > my_max ? v[u][e] : my_max;
               }
           }
         }
