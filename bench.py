@@ -32,9 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # The chunked forward selects through the fused indexer -> top-k path (dsa_index_topk) for
-# chunks whose first row sees at least this many pools, when k allows it; the same rule is
-# applied here to time the select the way the driver runs it.
+# chunks whose first row sees at least this many pools, when k allows it and the indexer has
+# more than 16 heads; the same rule is applied here to time the select the way the driver
+# runs it.
 FUSED_MIN_VISIBLE = 49152
+FUSED_MIN_HEADS = 17
 FUSED_MAX_K = 2730
 
 PEAK_HBM_GBS = 8000.0
@@ -189,7 +191,8 @@ def measure(wl, steps, warmup, args, dev):
     chunks = chunk_ranges(n, chunk)
 
     def uses_fused(t0):
-        return sel_ws is not None and min(p, (t0 + 1) // 4) >= FUSED_MIN_VISIBLE
+        return (sel_ws is not None and wl.h_i >= FUSED_MIN_HEADS and
+                min(p, (t0 + 1) // 4) >= FUSED_MIN_VISIBLE)
 
     def step_select(rec):
         """The select of every chunk as the chunked driver runs it (events per chunk when
@@ -302,8 +305,9 @@ def measure(wl, steps, warmup, args, dev):
         "fused_ms_per_step": sel_fused, "score_row_ms_per_step": sel_two,
         "tokens_per_s": n / ((sel_fused + sel_two) * 1e-3),
         "note": "indexer + top-k of every chunk as dsa_forward_chunked runs them: the fused "
-                "select (dsa_index_topk) on chunks whose rows see >= %d pools, else "
-                "dsa_index_scores + dsa_topk (the two phases above)" % FUSED_MIN_VISIBLE}
+                "select (dsa_index_topk) on chunks whose rows see >= %d pools when the "
+                "indexer has >= %d heads, else dsa_index_scores + dsa_topk (the two phases "
+                "above)" % (FUSED_MIN_VISIBLE, FUSED_MIN_HEADS)}
     if has_attn:
         phases["attn_fwd"] = {
             "ms_per_step": per_step["attn_fwd"], "avg_launch_ms": per_step["attn_fwd"] / n_launch,

@@ -276,9 +276,10 @@ dsa_status dsa_pool_keys(const void* x, int64_t ld_x, const float* gate, int64_t
 
 /*
  * dsa_forward_chunked - the whole DSA forward over n_tokens queries, one query chunk at a
- * time: for each chunk [t0, t0 + chunk) it runs the select (dsa_index_topk when k <= 2730,
- * else dsa_index_scores into one reused fp32 score buffer in the workspace and dsa_topk),
- * then dsa_sparse_attn_fwd.  Source: page
+ * time: for each chunk [t0, t0 + chunk) it runs the select (dsa_index_topk on chunks whose
+ * first row sees at least 49152 pools when k <= 2730 and h_i > 16, else dsa_index_scores
+ * into one reused fp32 score buffer in the workspace and dsa_topk; the indices are the same
+ * either way), then dsa_sparse_attn_fwd.  Source: page
  * "SkyRL ... 1 million tokens", section "Four optimizations", item 1 (indexer scores
  * computed in chunks per query, so the quadratic score matrix never exists beyond one
  * chunk).  Results do not depend on `chunk`.

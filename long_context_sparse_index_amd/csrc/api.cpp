@@ -124,6 +124,10 @@ constexpr int kSampleShift = 4;
 // many pools; on shorter rows the score-row select is as fast (measured on MI355X: the
 // candidate top-k's fixed per-row work then outweighs the score traffic it saves).
 constexpr int64_t kFusedMinVisible = 49152;
+// ... and only with more indexer heads than this: with at most 16 heads the score pass keeps
+// its key rows across tile groups (which the candidate pass does not), and the score-row
+// select is the faster one (1M tokens at 8 heads: 706 against 747 ms per forward step).
+constexpr int kFusedMinHeads = 17;
 
 struct FusedLayout {
   size_t sample, cand, t_est, cnt, fail, any, scores, total;
@@ -501,7 +505,8 @@ dsa_status dsa_forward_chunked(const void* q_idx, int64_t q_row_stride, const vo
     const void* q_idx_c = static_cast<const char*>(q_idx) + t0 * q_row_stride * ielt;
     int32_t* idx_chunk = idx_out ? idx_out + t0 * k : idx_ws;
     hipError_t e;
-    if (fused && std::min<int64_t>(n_pools, (t0 + 1) / 4) >= kFusedMinVisible) {
+    if (fused && h_i >= kFusedMinHeads &&
+        std::min<int64_t>(n_pools, (t0 + 1) / 4) >= kFusedMinVisible) {
       e = run_fused_select(q_idx_c, q_row_stride, k_idx, k_row_stride, w + t0 * w_row_stride,
                            w_row_stride, h_i, d_i, idx_dtype, t0, nq, n_pools, k, idx_chunk,
                            rest, s);

@@ -168,8 +168,9 @@ def test_fused_select_rejects(gpu):
 
 
 def test_chunked_forward_mixes_fused_and_two_call_chunks(gpu):
-    """dsa_forward_chunked takes the fused select only on chunks whose first row sees at
-    least 49152 pools: with P = 52000 and chunks of 50000 queries only the last chunk does.
+    """dsa_forward_chunked takes the fused select only with more than 16 indexer heads and on
+    chunks whose first row sees at least 49152 pools: with 24 heads, P = 52000 and chunks of
+    50000 queries only the last chunk does.
     Indices of every row must equal the two-call path, and the attention output is then the
     same kernel on the same indices (bit-identical)."""
     from long_context_sparse_index_amd import workloads as W
@@ -177,7 +178,7 @@ def test_chunked_forward_mixes_fused_and_two_call_chunks(gpu):
     say("case: chunked forward, P=52000, chunk 50000 (last chunk fused)")
     base = W.WORKLOADS["tiny_4k"]
     p = 52000
-    wl = W.Workload(name="mixed", n_tokens=4 * p, n_pools=p, h_i=4, d_i=64,
+    wl = W.Workload(name="mixed", n_tokens=4 * p, n_pools=p, h_i=24, d_i=64,
                     index_dtype="bf16", int_range=4, w_period=4, topk=2048, heads=8,
                     d_qk=128, d_v=128, scale=base.scale, chunk=50000)
     q_i, k_i, w = I.index_inputs(wl, gpu)
