@@ -25,8 +25,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 # Per-file device options.  The indexer's MFMA accumulators feed a VALU epilogue after every
-# head; in VGPRs (instead of accumulation registers) they need no copy-out first.
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# head; in VGPRs (instead of accumulation registers) they need no copy-out first.  The same
+# form lets the attention forward's register allocator keep each accumulator in one place
+# across the pipelined loop (with the default form it moves accumulators between
+# accumulation registers on some loop shapes).
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -230,9 +230,15 @@ struct TileDma {
 // instruction covers 8 rows x 128 contiguous bytes (eight whole cache lines of the 1152-byte
 // latent rows) instead of 32 rows x 32 bytes.  Layout of a tile:
 //   [key / 8][band][key % 8][position] x 16 bytes, chunk c of a band at position
-//   (c % 8) ^ swz(key), swz(key) = (key >> 1) & 7,
-// so the 16 keys read together by an MFMA operand load fall on 16 distinct 16-byte slots of
-// the 256-byte bank window.  DEPTH tiles are staged (see TileDma for the waits).
+//   (c % 8) ^ swz(key), swz(key) = 2 ((key >> 1) % 4) + (key >> 3) % 2.
+// Rows key and key + 1 sit 128 bytes apart, i.e. in the two halves of the 256-byte window of
+// the 64 LDS banks, and the swizzle takes the 8 even (or odd) keys of an aligned 16 onto 8
+// distinct 16-byte positions: the 16 keys of a key-row operand load (one chunk each) hit 16
+// distinct slots.  The transposed value reads take two adjacent chunks (32 bytes) of each of
+// 8 consecutive keys per 256 bytes of data; their swizzles differ in bits 1-2 among the 4
+// even (or odd) keys of an aligned 8, so the chunk pairs are disjoint and those reads are
+// conflict-free too (with (key >> 1) & 7 keys k and k + 2 shared a pair: two-way conflicts).
+// DEPTH tiles are staged (see TileDma for the waits).
 template <int DQK, int DV, bool SEPARATE_V, int DEPTH>
 struct TileDmaBands {
   static constexpr int kChunksQK = DQK / 8;
@@ -247,7 +253,9 @@ struct TileDmaBands {
   static_assert(kAttnThreads == 256, "four waves of 8 keys");
   static_assert(DEPTH >= 1 && DEPTH <= 3 && kPerWave * (DEPTH - 1) < 64, "vmcnt range");
 
-  __device__ __forceinline__ static int swz(int key) { return (key >> 1) & 7; }
+  __device__ __forceinline__ static int swz(int key) {
+    return (((key >> 1) & 3) << 1) | ((key >> 3) & 1);
+  }
 
   // Byte offset in a tile of chunk `c` (columns [8c, 8c + 8)) of tile key `key`.
   __device__ __forceinline__ static int offset(int key, int c) {
@@ -264,31 +272,36 @@ struct TileDmaBands {
     return sel[slot];
   }
 
-  // Issues the loads of the tile whose row for this lane is `p` into stage `stage`.
-  __device__ __forceinline__ static void issue_row(uint8_t* tiles, int stage, int64_t p,
-                                                   const uint16_t* __restrict__ kv,
-                                                   int64_t ld_kv,
-                                                   const uint16_t* __restrict__ v,
-                                                   int64_t ld_v) {
+  // Issues the load of band `b` (columns [64 b, 64 b + 64) of the row) of the tile whose row
+  // for this lane is `p` into stage `stage`: one instruction, 1 KB of LDS per wave.
+  __device__ __forceinline__ static void issue_band(uint8_t* tiles, int stage, int64_t p, int b,
+                                                    const uint16_t* __restrict__ kv,
+                                                    int64_t ld_kv,
+                                                    const uint16_t* __restrict__ v,
+                                                    int64_t ld_v) {
     const int lane = threadIdx.x & 63;
     // Wave-uniform: keeps the LDS destinations (M0) in scalar registers.
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int key = 8 * wid + (lane >> 3);
     const int pos = (lane & 7) ^ swz(key);  // chunk of each band this lane loads
     const uint32_t base = lds_addr_of(tiles) + stage * kTileBytes + wid * kGroupBytes;
-    if constexpr (!SEPARATE_V) {
-      const uint16_t* rowp = kv + p * ld_kv + pos * 8;
+    const int c = 8 * b + pos;
+    const uint16_t* src;
+    if constexpr (!SEPARATE_V)
+      src = kv + p * ld_kv + c * 8;
+    else
+      src = c < kChunksQK ? kv + p * ld_kv + c * 8 : v + p * ld_v + (c - kChunksQK) * 8;
+    dma_16b(src, base + b * 1024);
+  }
+
+  // Issues all loads of the tile whose row for this lane is `p` into stage `stage`.
+  __device__ __forceinline__ static void issue_row(uint8_t* tiles, int stage, int64_t p,
+                                                   const uint16_t* __restrict__ kv,
+                                                   int64_t ld_kv,
+                                                   const uint16_t* __restrict__ v,
+                                                   int64_t ld_v) {
 #pragma unroll
-      for (int b = 0; b < kBands; ++b) dma_16b(rowp + b * 64, base + b * 1024);
-    } else {
-#pragma unroll
-      for (int b = 0; b < kBands; ++b) {
-        const int c = 8 * b + pos;
-        const uint16_t* src =
-            c < kChunksQK ? kv + p * ld_kv + c * 8 : v + p * ld_v + (c - kChunksQK) * 8;
-        dma_16b(src, base + b * 1024);
-      }
-    }
+    for (int b = 0; b < kBands; ++b) issue_band(tiles, stage, p, b, kv, ld_kv, v, ld_v);
   }
 
   __device__ __forceinline__ static void issue(uint8_t* tiles, int stage, int t,

@@ -437,9 +437,10 @@ void attn_fwd_pair_kernel(
   };
   auto fused_step = [&](int st_k, int st_v, int t1, const Ahead& ah, const bf16x8 (&phi)[2],
                         const bf16x8 (&plo)[2], float (&l_run)[2], float (&ymax)[2],
-                        auto split) {
+                        int st_d, int32_t row_d, auto split) {
     constexpr bool SPLIT = decltype(split)::value;
     static_assert(kKS % 2 == 0 && kKS / 2 <= kNBH, "pipeline shape");
+    static_assert(Dma::kBands <= kKS, "one gather band per phase-1 slot");
     // P.V blocks in phase 1: SPLIT, half a block (two MFMAs) in each of the first 2 kN1
     // slots; otherwise one whole block (two MFMAs) in each of the first kN1s slots.
     constexpr int kN1s = kPvPhase1Single < kKS
@@ -459,6 +460,11 @@ void attn_fwd_pair_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kKS; ++j) {
+      // The gather of the tile two ahead (row row_d of this lane, stage st_d): band j in slot
+      // j.  Issued as one burst after the barrier, its loads held up the wave (5-8% of the
+      // kernel at 128k); one per slot, the memory pipeline works through them beside the
+      // MFMA work.
+      if (j < Dma::kBands) Dma::issue_band(tiles, st_d, row_d, j, kv, ld_kv, v, ld_v);
       if (j + 2 < kKS) ka[(j + 2) % 3] = lds_load_bf16x8(kb[j & 1] + ((j + 2) >> 1) * 1024);
       if constexpr (SPLIT) {
         const int n = j / 2;
@@ -588,19 +594,24 @@ void attn_fwd_pair_kernel(
     if constexpr (DO_PV) {
       if (compute) read_probabilities(0, phi, plo, split);
     }
-    if (n_tiles > 2) Dma::issue(tiles, 2, 2, sel, n_valid, kv, ld_kv, v, ld_v);
+    // The max pass gathers tile t + 3 after the barrier of tile t; the P.V pass gathers tile
+    // t + 2 during the fused step of tile t, into the stage freed at the previous barrier.
+    if (!DO_PV && n_tiles > 2) Dma::issue(tiles, 2, 2, sel, n_valid, kv, ld_kv, v, ld_v);
     int st_cur = 0, st_next = 1, st_after = 2;  // stages of tiles t, t + 1, t + 2
     Ahead ah;
     if constexpr (DO_PV) {
       if (compute && n_tiles > 1) read_ahead(st_next, st_cur, ah);
     }
     for (int t = 0; t + 1 < n_tiles; ++t) {
-      // Row of the tile three ahead (clamped, so always a valid read), read now so that the
-      // load issue after the barrier does not wait for LDS.
-      const int32_t row3 = Dma::row_of(t + 3, sel, n_valid);
+      // Row of the tile gathered in this iteration (clamped, so always a valid read; past the
+      // last tile the P.V pass reloads a valid row into the free stage, which nothing reads).
+      const int32_t row_g = Dma::row_of(t + (DO_PV ? 2 : 3), sel, n_valid);
+      if constexpr (DO_PV) {
+        if (!compute) Dma::issue_row(tiles, st_after, row_g, kv, ld_kv, v, ld_v);
+      }
       if (compute) {
         if constexpr (DO_PV) {
-          fused_step(st_next, st_cur, t + 1, ah, phi, plo, l_run, ymax, split);
+          fused_step(st_next, st_cur, t + 1, ah, phi, plo, l_run, ymax, st_after, row_g, split);
         } else {
           logits(st_next, s);
           shifted(s, t + 1, zero_m, y);
@@ -617,7 +628,7 @@ void attn_fwd_pair_kernel(
           if (t + 2 < n_tiles) read_ahead(st_after, st_next, ah);
         }
       }
-      if (t + 3 < n_tiles) Dma::issue_row(tiles, st_cur, row3, kv, ld_kv, v, ld_v);
+      if (!DO_PV && t + 3 < n_tiles) Dma::issue_row(tiles, st_cur, row_g, kv, ld_kv, v, ld_v);
       const int st_free = st_cur;
       st_cur = st_next;
       st_next = st_after;
