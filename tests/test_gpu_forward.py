@@ -339,6 +339,13 @@ def test_attention_latent_576_random_selection(gpu, h):
     idx[1, :] = -1
     idx[1, 5] = 17  # a row with one valid slot
     idx[2, 33:] = -1  # a partial last tile
+    # Rows whose gathers run past the last tile (the tile two ahead is reloaded from a valid
+    # row into the free stage): exactly 2 and 3 tiles, 3 and 4 tiles with one key in the
+    # last; and the two sides of the probability-precision boundary (512 valid slots).
+    for r, n_keep in [(3, 64), (4, 65), (5, 96), (6, 97), (7, 511), (8, 512)]:
+        keep = perm[r, :n_keep].to(torch.int32)
+        idx[r, :] = -1
+        idx[r, k - n_keep:] = keep  # valid slots at the end of the row: compaction matters
     scale = 1.0 / 24.0
     o, lse = B.sparse_attn_fwd_new(q, kv, idx, scale=scale, d_v=512)
     torch.cuda.synchronize()
