@@ -105,6 +105,18 @@ __device__ __forceinline__ uint32_t wave_append(uint32_t cnt, uint32_t* len) {
   return base + incl - cnt;
 }
 
+// As above, and also returns in *end the end of the wave's reservation (wave-uniform).
+__device__ __forceinline__ uint32_t wave_append(uint32_t cnt, uint32_t* len, uint32_t* end) {
+  const uint32_t incl = wave_inclusive_scan(cnt);
+  const uint32_t total =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  uint32_t base = 0u;
+  if (total != 0u && (threadIdx.x & 63) == 63) base = atomicAdd(len, total);
+  base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), 63));
+  *end = base + total;
+  return base + incl - cnt;
+}
+
 // Value of lane (lane ^ LS) of the wave, by VALU cross-lane moves: DPP quad permutes for 1
 // and 2, a half-row mirror (lane ^ 7) then a quad reversal (lane ^ 3) for 4, a row rotation
 // by 8 for 8, and the gfx950 row and half-wave swaps for 16 and 32.
@@ -418,10 +430,11 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
 
   // Ranking sort of the n entries of buf[0, n) (distinct composites (~key << 32) | pool)
   // into ascending order, i.e. score descending, lower pool first among equal scores.
-  // nlo <= nhi bound the entries' ~key.  Each entry goes to one of kRankBuckets buckets by a
-  // function of ~key that never decreases as ~key grows (a linear map of ~key - nlo in
-  // fp32, truncated), so every entry of a lower bucket sorts before every entry of a higher
-  // one; a block scan of the bucket counts gives each bucket's first position, and an
+  // nlo <= nhi span the entries' ~key: nhi bounds it from above, and entries below nlo
+  // share the first bucket.  Each entry goes to one of kRankBuckets buckets by a function
+  // of ~key that never decreases as ~key grows (0 below nlo, then a linear map of
+  // ~key - nlo in fp32, truncated), so every entry of a lower bucket sorts before every
+  // entry of a higher one; a block scan of the bucket counts gives each bucket's first position, and an
   // entry's position is its bucket's start plus the number of entries of its bucket below
   // it (exact 64-bit compares).  Scores near a selection threshold spread a few entries per
   // bucket, so this costs a few LDS reads per entry instead of a sorting network's 66
@@ -438,7 +451,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
                                 : 0.f;
     auto bucket = [&](uint64_t x) {
       const uint32_t nk = static_cast<uint32_t>(x >> 32);
-      const uint32_t b = static_cast<uint32_t>(static_cast<float>(nk - nlo) * inv);
+      const uint32_t b =
+          nk > nlo ? static_cast<uint32_t>(static_cast<float>(nk - nlo) * inv) : 0u;
       return b < static_cast<uint32_t>(kRankBuckets - 1) ? b
                                                          : static_cast<uint32_t>(kRankBuckets - 1);
     };
@@ -507,8 +521,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
   };
 
   // Writes the first min(k, n) of the n entries of buf[0, n) (n <= kMaxK) to the output row
-  // in sorted order, -1 in the slots past n.  nlo <= nhi bound the entries' ~key, or nlo >
-  // nhi to have them found here.  The ranking sort, or for heavy ties the bitonic network
+  // in sorted order, -1 in the slots past n.  nlo <= nhi span the entries' ~key (as in the
+  // ranking sort), or nlo > nhi to have them found here.  The ranking sort, or for heavy ties the bitonic network
   // over buf padded with ~0 to a power of two.  All threads call it after writing buf.
   auto sort_and_store = [&](int n, uint32_t nlo, uint32_t nhi, bool raw = false)
                             __attribute__((always_inline)) {
@@ -763,11 +777,15 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       // One pass over the row: every score whose key is at or above lower is listed as
       // (score bits << 32) | pool, kListF4 float4 per thread in flight, one list reservation
       // per wave and pass.  Scores are compared as floats against the smallest float of key
-      // lower (-inf when lower is below the key of -inf).
+      // lower (-inf when lower is below the key of -inf).  A wave whose groups of a round all
+      // lie inside the row (every round but the one holding the row's end) skips the
+      // per-element visibility test, and a wave whose reservation ends past the list's
+      // capacity stores nothing (the row then fails the size test below).
       const float f_lower =
           lower <= 0x007FFFFFu ? -__builtin_inff()
                                : __uint_as_float((lower & 0x80000000u) ? lower ^ 0x80000000u : ~lower);
-      float my_max = -__builtin_inff();  // largest listed score
+      const int wfirst = __builtin_amdgcn_readfirstlane(tid & ~63);
+      uint32_t* const buf32 = reinterpret_cast<uint32_t*>(buf);
       for (int base = 0; base < n4; base += kListF4 * kTopkThreads) {
         f32x4 v[kListF4];
 #pragma unroll
@@ -776,42 +794,58 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
           v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
                          : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // Visible elements of this lane's group in round u (4 when the wave's round is whole).
+        auto n_visible = [&](int u) {
+          return min(max(vis - 4 * (base + u * kTopkThreads + tid), 0), 4);
+        };
+        auto whole = [&](int u) { return 4 * (base + u * kTopkThreads + wfirst + 64) <= vis; };
+        auto present = [&](int u) { return base + u * kTopkThreads + wfirst < n4; };
         uint32_t cnt = 0u;
 #pragma unroll
         for (int u = 0; u < kListF4; ++u) {
-          if (base + u * kTopkThreads < n4) {  // uniform
-            const int nv = min(max(vis - 4 * (base + u * kTopkThreads + tid), 0), 4);
+          if (!present(u)) continue;  // uniform
+          if (whole(u)) {             // uniform
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cnt += v[u][e] >= f_lower ? 1u : 0u;
+          } else {
+            const int nv = n_visible(u);
 #pragma unroll
             for (int e = 0; e < 4; ++e) cnt += e < nv && v[u][e] >= f_lower ? 1u : 0u;
           }
         }
-        uint32_t slot = wave_append(cnt, &fill[1]);
+        uint32_t end;
+        const uint32_t slot = wave_append(cnt, &fill[1], &end);
+        if (end > static_cast<uint32_t>(kCand)) continue;  // uniform
+        uint32_t* a = buf32 + 2u * slot;  // the lane's next entry: pool, then score bits
+        auto put = [&](uint32_t pool, float x) {
+          a[0] = pool;
+          a[1] = __float_as_uint(x);
+          a += 2;
+        };
 #pragma unroll
         for (int u = 0; u < kListF4; ++u) {
-          if (base + u * kTopkThreads < n4) {  // uniform
-            const int i4 = base + u * kTopkThreads + tid;
-            const int nv = min(max(vis - 4 * i4, 0), 4);
+          if (!present(u)) continue;
+          const uint32_t i0 = static_cast<uint32_t>(4 * (base + u * kTopkThreads + tid));
+          if (whole(u)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (e < nv && v[u][e] >= f_lower) {
-                if (slot < static_cast<uint32_t>(kCand))
-                  buf[slot] = (static_cast<uint64_t>(__float_as_uint(v[u][e])) << 32) |
-                              static_cast<uint32_t>(4 * i4 + e);
-                ++slot;
-                my_max = v[u][e] > my_max ? v[u][e] : my_max;
-              }
+              if (v[u][e] >= f_lower) put(i0 + e, v[u][e]);
+          } else {
+            const int nv = n_visible(u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e < nv && v[u][e] >= f_lower) put(i0 + e, v[u][e]);
           }
         }
       }
-      // Keys of listed scores are >= lower > 0; a thread that listed none contributes 0.
-      const uint32_t max_key = wave_max_u32(my_max >= f_lower ? score_key(my_max) : 0u);
-      if (lane == 0 && max_key) atomicMax(&cand_max, max_key);
       __syncthreads();
       const uint32_t n_cand = fill[1];
       if (n_cand < static_cast<uint32_t>(k) || n_cand > static_cast<uint32_t>(kCand))
         return false;
-      // The listed keys lie in [lower, cand_max]; the entries hold raw scores.
-      sort_and_store(static_cast<int>(n_cand), ~cand_max, ~lower, true);
+      // The listed keys are at least lower; the sample's largest key bounds all but a few
+      // of them from above (the ranking sort puts any larger key in its first bucket).  The
+      // entries hold raw scores.
+      sort_and_store(static_cast<int>(n_cand), ~khi, ~lower, true);
       return true;
     }
   };
