@@ -249,31 +249,41 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   // L = wid + 4 i (if L < kDmaPerHead); lane slot s = 64 L + lane -> row s / kCpr, position
   // s % kCpr.
   // One tile: the loads' source rows are fixed, so their addresses are formed once.
-  int dma_row[kDmaPerWave];
-  int dma_chunk[kDmaPerWave];
+  auto dma_row = [&](int i) {  // loads past the tile (not issued) stay in range
+    return ((64 * (wid + kIdxWaves * i) + lane) / kCpr) % kBQ;
+  };
+  auto dma_chunk = [&](int i) {
+    return ((64 * (wid + kIdxWaves * i) + lane) % kCpr) ^ swz(dma_row(i));
+  };
+  // Several tiles: with a short row stride, a whole tile's loads sit at fixed 32-bit lane
+  // offsets from the tile's first row (dma_off), so that a pass adds only a wave-uniform
+  // base; the last, partial tile of the range (or a long stride) clamps its rows instead.
+  const bool short_stride = q_stride_b * kBQ < (int64_t{1} << 31);
   const uint8_t* dma_src[kDmaPerWave];
+  uint32_t dma_off[kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
-    const int slot = 64 * (wid + kIdxWaves * i) + lane;
-    const int row = (slot / kCpr) % kBQ;  // loads past the tile (not issued) stay in range
-    dma_row[i] = row;
-    dma_chunk[i] = (slot % kCpr) ^ swz(row);
-    const int64_t t = qt_first * kBQ + row;
-    dma_src[i] = q + (t < nq ? t : nq - 1) * q_stride_b + dma_chunk[i] * 16;  // any valid row
+    const int64_t t = qt_first * kBQ + dma_row(i);
+    dma_src[i] = q + (t < nq ? t : nq - 1) * q_stride_b + dma_chunk(i) * 16;  // any valid row
+    dma_off[i] = static_cast<uint32_t>(short_stride ? dma_row(i) * q_stride_b : 0) +
+                 dma_chunk(i) * 16;
   }
   const uint32_t q_lds_a = lds_addr_of(q_lds);
-  auto issue = [&](int jj) {
-    const int qi = MULTI ? jj / h_i : 0;
-    const int j = jj - qi * h_i;
+  // Loads of pass jj = qi * h_i + j (query tile qi of the block, head j).
+  auto issue = [&](int jj, int qi, int j) {
     const int64_t t0 = (qt_first + qi) * kBQ;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i)
       if (wid + kIdxWaves * i < kDmaPerHead) {
         const uint32_t dst = q_lds_a + (jj % kStages) * kHeadBytes + (wid + kIdxWaves * i) * 1024;
         if constexpr (MULTI) {
-          const int64_t t = t0 + dma_row[i];
-          idx_dma_16b(q + (t < nq ? t : nq - 1) * q_stride_b + j * kRowBytes + dma_chunk[i] * 16,
-                      dst);
+          if (short_stride && t0 + kBQ <= nq) {  // wave-uniform: every row of the tile exists
+            idx_dma_16b(q + (t0 * q_stride_b + j * kRowBytes) + dma_off[i], dst);
+          } else {
+            const int64_t t = t0 + dma_row(i);
+            idx_dma_16b(
+                q + (t < nq ? t : nq - 1) * q_stride_b + j * kRowBytes + dma_chunk(i) * 16, dst);
+          }
         } else {
           idx_dma_16b(dma_src[i] + static_cast<int64_t>(j) * kRowBytes, dst);
         }
@@ -281,7 +291,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   };
 
   f32x4 sc[kMB][NB];
-  for (int jj = 0; jj < kStages - 1 && jj < n_pass; ++jj) issue(jj);
+  for (int jj = 0; jj < kStages - 1 && jj < n_pass; ++jj)
+    issue(jj, MULTI ? jj / h_i : 0, MULTI ? jj % h_i : jj);
+  // Tile and head of the next pass to issue, advanced one pass at a time.
+  int ia_q = MULTI ? (kStages - 1) / h_i : 0;
+  int ia_j = MULTI ? (kStages - 1) % h_i : kStages - 1;
   // The key rows and the first passes' loads land together.  Waiting for them here, once,
   // also tells the compiler that the key registers are complete before the pass loop;
   // otherwise it would wait for every outstanding load (the prefetched passes included) at
@@ -311,7 +325,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();  // pass jj's tile is in LDS for every wave; jj - 1 read
       asm volatile("" ::: "memory");
-      if (jj + kStages - 1 < n_pass) issue(jj + kStages - 1);
+      if (jj + kStages - 1 < n_pass) {
+        issue(jj + kStages - 1, ia_q, ia_j);
+        if (MULTI && ++ia_j == h_i) {
+          ia_j = 0;
+          ++ia_q;
+        }
+        if (!MULTI) ++ia_j;
+      }
       if (wave_live) {
         const lds_ptr stage = qb + (jj % kStages) * kHeadBytes;
         f32x4 acc[kMB][NB];
