@@ -335,44 +335,82 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       }
       if (wave_live) {
         const lds_ptr stage = qb + (jj % kStages) * kHeadBytes;
-        f32x4 acc[kMB][NB];
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          Frag qf[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int row = nb * 16 + r16;
-            const int c0 = (ks * kStepBytes + g * kFragBytes) / 16;
-            if constexpr (FP8) {
-              const u32x4 lo =
-                  *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                      stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
-              const u32x4 hi =
-                  *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                      stage + row * kRowBytes + (((c0 + 1) ^ swz(row)) * 16));
-              for (int e = 0; e < 4; ++e) {
-                qf[nb][e] = lo[e];
-                qf[nb][4 + e] = hi[e];
-              }
-            } else {
-              qf[nb] = lds_load_bf16x8(stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+        // Query fragment of step ks, column block nb (B operand: query nb * 16 + r16).
+        auto read_q = [&](int ks, int nb) {
+          const int row = nb * 16 + r16;
+          const int c0 = (ks * kStepBytes + g * kFragBytes) / 16;
+          Frag f;
+          if constexpr (FP8) {
+            const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+            const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                stage + row * kRowBytes + (((c0 + 1) ^ swz(row)) * 16));
+            for (int e = 0; e < 4; ++e) {
+              f[e] = lo[e];
+              f[4 + e] = hi[e];
             }
+          } else {
+            f = lds_load_bf16x8(stage + row * kRowBytes + ((c0 ^ swz(row)) * 16));
+          }
+          return f;
+        };
+        f32x4 acc[kMB][NB];
+        auto head_epilogue = [&](int mb, int nb, float wv) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
+        };
+        if constexpr (MULTI || FP8) {
+          // All pool blocks advance together, one contraction step at a time (the step's
+          // query fragments live only through it).
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks) {
+            Frag qf[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) qf[nb] = read_q(ks, nb);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)  // the first step starts from a literal zero
+                acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
+                                             ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
           }
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
+          for (int nb = 0; nb < NB; ++nb) {
+            const float wv = w_lds[jj * kBQ + nb * 16 + r16];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)  // the first step starts from a literal zero
-              acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
-                                           ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
-        }
+            for (int mb = 0; mb < kMB; ++mb) head_epilogue(mb, nb, wv);
+          }
+        } else {
+          // bf16, single tiles: pool blocks in pairs.  A pair's products finish after its own
+          // MFMAs (2 NB independent chains), so its ReLU + weight epilogue overlaps the next
+          // pair's MFMAs (2-3% faster with 32 heads).  The query fragments of every step stay
+          // live through the pass, which tile groups cannot afford (a wave per SIMD); on fp8
+          // (one step per head) the order measured 1-2% slower.
+          static_assert(kMB % 2 == 0, "pool blocks in pairs");
+          Frag qf[kKS][NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const float wv = w_lds[jj * kBQ + nb * 16 + r16];
+          for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
+            for (int nb = 0; nb < NB; ++nb) qf[ks][nb] = read_q(ks, nb);
+          float wv[NB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
+          for (int nb = 0; nb < NB; ++nb) wv[nb] = w_lds[jj * kBQ + nb * 16 + r16];
+#pragma unroll
+          for (int mp = 0; mp < kMB; mp += 2) {
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+              for (int mb = mp; mb < mp + 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                  acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[ks][nb],
+                                               ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
+#pragma unroll
+            for (int mb = mp; mb < mp + 2; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) head_epilogue(mb, nb, wv[nb]);
+          }
         }
       }
     }
