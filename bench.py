@@ -89,10 +89,11 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel, workload):
+def recorded_traffic(kernel, workload, instance_suffix=None):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter profile
     (profiles/<kernel>_<workload>_traffic.md, a line 'traffic: {json}'), or None when there
-    is none or the kernel's sources changed since it was taken."""
+    is none, the kernel's sources changed since it was taken, or the recorded kernel instance
+    does not end in `instance_suffix` (e.g. the attention's output type parameter)."""
     path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -101,6 +102,8 @@ def recorded_traffic(kernel, workload):
             if line.startswith("traffic: "):
                 rec = json.loads(line[len("traffic: "):])
                 if rec.get("source_hash") != kernel_source_hash(kernel):
+                    return None
+                if instance_suffix and not rec.get("kernel", "").endswith(instance_suffix):
                     return None
                 return rec["bytes_per_launch"]
     return None
@@ -333,7 +336,8 @@ def measure(wl, steps, warmup, args, dev):
         ach = gbs(attn_bytes / n_launch, per_step["attn_fwd"] / n_launch)
         roof = {"kernel": "attn_fwd", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": recorded_traffic("attn_fwd", wl.name)}
+                "traffic": recorded_traffic(
+                    "attn_fwd", wl.name, ", true>" if wl.attn_out == "fp32" else ", false>")}
 
     if has_attn:
         phases["pool_keys"] = time_pool_keys(wl, dev, stream)

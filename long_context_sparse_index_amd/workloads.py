@@ -60,8 +60,9 @@ WORKLOADS = {
             name="fwd_128k",
             n_tokens=131072, n_pools=32768, h_i=32, d_i=128, index_dtype="bf16", int_range=4,
             w_period=4, topk=2048, heads=64, d_qk=576, d_v=512, scale=_s(576), chunk=8192,
+            attn_out="bf16",
             description="DSA forward at 128k tokens: 32x128 bf16 indexer, top-2048, 64-head "
-                        "sparse MQA over 576/512 latent rows, chunk 8192"),
+                        "sparse MQA over 576/512 latent rows, chunk 8192; O in bf16"),
         Workload(
             name="index_topk_256k_fp8",
             n_tokens=262144, n_pools=65536, h_i=32, d_i=128, index_dtype="fp8", int_range=8,
@@ -87,8 +88,10 @@ WORKLOADS = {
             name="flash_nope_128k",
             n_tokens=131072, n_pools=32768, h_i=32, d_i=128, index_dtype="bf16", int_range=4,
             w_period=4, topk=2051, heads=64, d_qk=512, d_v=512, scale=_s(512), chunk=8192,
+            attn_out="bf16",
             description="DSA forward at 128k with Flash-native shapes: top-2051 and 64-head "
-                        "sparse MQA over 512-wide NoPE latent rows (no padding to 576/512)"),
+                        "sparse MQA over 512-wide NoPE latent rows (no padding to 576/512); "
+                        "O in bf16"),
         Workload(
             name="tp_share_1m",
             n_tokens=1048576, n_pools=262144, h_i=8, d_i=128, index_dtype="bf16", int_range=4,
