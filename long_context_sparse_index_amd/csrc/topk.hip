@@ -434,11 +434,11 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
   // share the first bucket.  Each entry goes to one of kRankBuckets buckets by a function
   // of ~key that never decreases as ~key grows (0 below nlo, then a linear map of
   // ~key - nlo in fp32, truncated), so every entry of a lower bucket sorts before every
-  // entry of a higher one; a block scan of the bucket counts gives each bucket's first position, and an
-  // entry's position is its bucket's start plus the number of entries of its bucket below
-  // it (exact 64-bit compares).  Scores near a selection threshold spread a few entries per
-  // bucket, so this costs a few LDS reads per entry instead of a sorting network's 66
-  // compare-exchange steps.  The pools of the first min(n, k) positions are left, in
+  // entry of a higher one; a block scan of the bucket counts gives each bucket's first
+  // position, and an entry's position is its bucket's start plus the number of entries of
+  // its bucket below it (exact 64-bit compares).  Scores near a selection threshold spread
+  // a few entries per bucket, so this costs a few LDS reads per entry instead of a sorting
+  // network's 66 compare-exchange steps.  The pools of the first min(n, k) positions are left, in
   // order, in the first words of buf.  Returns false, with buf untouched, when a bucket
   // holds more than kRankMaxBucket entries (heavy ties).  rbin and rrange[2] are zero on
   // entry; cand is free.
@@ -522,8 +522,9 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
 
   // Writes the first min(k, n) of the n entries of buf[0, n) (n <= kMaxK) to the output row
   // in sorted order, -1 in the slots past n.  nlo <= nhi span the entries' ~key (as in the
-  // ranking sort), or nlo > nhi to have them found here.  The ranking sort, or for heavy ties the bitonic network
-  // over buf padded with ~0 to a power of two.  All threads call it after writing buf.
+  // ranking sort), or nlo > nhi to have them found here.  The ranking sort, or for heavy
+  // ties the bitonic network over buf padded with ~0 to a power of two.  All threads call
+  // it after writing buf.
   auto sort_and_store = [&](int n, uint32_t nlo, uint32_t nhi, bool raw = false)
                             __attribute__((always_inline)) {
     if (n == 0) {
