@@ -37,7 +37,7 @@ constexpr int kMaxHeads = 64;
 // Few-head score launches (at most kMaxGroupHeads heads): (query tile, head) passes per
 // block's key-row load at most, and the grid size below which blocks take fewer query tiles.
 constexpr int kMaxGroupHeads = 16;
-constexpr int kPassesPerKeyLoad = 128;
+constexpr int kPassesPerKeyLoad = 256;
 constexpr int kMinBlocks = 2048;
 
 template <bool FP8>
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
           for (int i = 0; i < 4; ++i)
             sc[mb][nb][i] = __builtin_fmaf(wv, relu_bits(acc[mb][nb][i]), sc[mb][nb][i]);
         };
-        if constexpr (MULTI || FP8) {
+        if constexpr ((MULTI && NB > 1) || FP8) {
           // All pool blocks advance together, one contraction step at a time (the step's
           // query fragments live only through it).
 #pragma unroll
@@ -382,11 +382,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
             for (int mb = 0; mb < kMB; ++mb) head_epilogue(mb, nb, wv);
           }
         } else {
-          // bf16, single tiles: pool blocks in pairs.  A pair's products finish after its own
-          // MFMAs (2 NB independent chains), so its ReLU + weight epilogue overlaps the next
-          // pair's MFMAs (2-3% faster with 32 heads).  The query fragments of every step stay
-          // live through the pass, which tile groups cannot afford (a wave per SIMD); on fp8
-          // (one step per head) the order measured 1-2% slower.
+          // bf16, single tiles and 16-row tile groups: pool blocks in pairs.  A pair's
+          // products finish after its own MFMAs (2 NB independent chains), so its ReLU +
+          // weight epilogue overlaps the next pair's MFMAs (2-3% faster with 32 heads).  The
+          // query fragments of every step stay live through the pass, which 32-row tile
+          // groups cannot afford (a wave per SIMD); on fp8 (one step per head) the order
+          // measured 1-2% slower.
           static_assert(kMB % 2 == 0, "pool blocks in pairs");
           Frag qf[kKS][NB];
 #pragma unroll
@@ -553,14 +554,16 @@ hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
 }
 
 // Tiles.  With few heads a block's key rows serve little MFMA work per load, so for score
-// output a block walks several consecutive 32-row query tiles (MULTI) with its key rows
+// output a block walks several consecutive 16-row query tiles (MULTI) with its key rows
 // resident and the query staging running on across tiles: up to kPassesPerKeyLoad (tile,
 // head) passes per key load, fewer tiles while the grid would hold fewer than kMinBlocks
-// blocks.  Measured at 8 heads against 64-row single tiles: 5-6% faster with 32 passes per
-// load, 12% with 64, 15% with 128; at 32 heads 6-8% slower (so up to 16 heads only).  Otherwise a block owns
-// one tile of 32 rows, or of 64 rows when few heads (at most 8) leave each block little MFMA
-// work per key-row load: the larger tile doubles the queries each key row serves (5% faster
-// at 8 heads, 3% slower at 32).  The 64-row tile and MULTI are kept to d_i <= 128, whose
+// blocks.  Measured at 8 heads against 64-row single tiles (with 32-row tiles): 5-6% faster
+// with 32 passes per load, 12% with 64, 15% with 128; at 32 heads 6-8% slower (so up to 16
+// heads only).  16-row tiles (128 VGPRs: four waves per SIMD, and the pool-pair MFMA order
+// fits) with 256 passes per load are another 2-3% faster at 1M than 32-row tiles with 128
+// (384 passes: 2% slower again).  Otherwise a block owns one tile of 32 rows, or of 64 rows
+// when few heads (at most 8) leave each block little MFMA work per key-row load: the larger
+// tile doubles the queries each key row serves (5% faster at 8 heads, 3% slower at 32).  The 64-row tile and MULTI are kept to d_i <= 128, whose
 // key, score and product registers still fit.  The candidate pass (its epilogue holds more
 // registers across a tile loop), the sampled pass of the fused select (1% slower with tile
 // groups) and launches that compute only flagged tiles take single tiles.
@@ -576,16 +579,17 @@ hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
   if (nq <= 0 || vis_max <= 0) return hipSuccess;
   const int64_t n_pool_tiles = (vis_max + kPoolsPerBlock - 1) / kPoolsPerBlock;
   const int64_t tiles32 = (nq + 31) / 32;
+  const int64_t tiles16 = (nq + 15) / 16;
   if constexpr (D <= 128) {
     const bool single = opt.gate_rows || opt.cand || opt.pool_shift != 0;
     int group_tiles = (single || h_i > kMaxGroupHeads) ? 1 : kPassesPerKeyLoad / h_i;
     while (group_tiles > 1 &&
-           ((tiles32 + group_tiles - 1) / group_tiles) * n_pool_tiles < kMinBlocks)
+           ((tiles16 + group_tiles - 1) / group_tiles) * n_pool_tiles < kMinBlocks)
       group_tiles /= 2;
     if (group_tiles > 1)
-      return launch_indexer_nb<D, 2, FP8, true>(q, q_row_stride, k, k_row_stride, w,
+      return launch_indexer_nb<D, 1, FP8, true>(q, q_row_stride, k, k_row_stride, w,
                                                 w_row_stride, scores, ld, q_start, nq, n_pools,
-                                                h_i, accumulate, opt, tiles32, n_pool_tiles,
+                                                h_i, accumulate, opt, tiles16, n_pool_tiles,
                                                 group_tiles, stream);
     if (h_i <= 8)
       return launch_indexer_nb<D, 4, FP8, false>(q, q_row_stride, k, k_row_stride, w,
