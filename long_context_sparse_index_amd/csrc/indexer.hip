@@ -561,9 +561,12 @@ hipError_t launch_indexer_nb(const void* q, int64_t q_row_stride, const void* k,
 // with 32 passes per load, 12% with 64, 15% with 128; at 32 heads 6-8% slower (so up to 16
 // heads only).  16-row tiles (128 VGPRs: four waves per SIMD, and the pool-pair MFMA order
 // fits) with 256 passes per load are another 2-3% faster at 1M than 32-row tiles with 128
-// (384 passes: 2% slower again).  Otherwise a block owns one tile of 32 rows, or of 64 rows
-// when few heads (at most 8) leave each block little MFMA work per key-row load: the larger
-// tile doubles the queries each key row serves (5% faster at 8 heads, 3% slower at 32).  The 64-row tile and MULTI are kept to d_i <= 128, whose
+// (384 passes: 2% slower again).  Otherwise a block owns one tile of 64 rows when few heads
+// (at most 8) leave each block little MFMA work per key-row load (the larger tile doubles
+// the queries each key row serves: 5% faster at 8 heads, 3% slower at 32), else one tile of
+// 16 rows for bf16 scores (120 VGPRs, four waves per SIMD: 2-3% faster at 32 heads than 32
+// rows at three waves; tile groups of them are 3-7% slower there) and of 32 rows for fp8
+// and the candidate pass.  The 64-row tile and MULTI are kept to d_i <= 128, whose
 // key, score and product registers still fit.  The candidate pass (its epilogue holds more
 // registers across a tile loop), the sampled pass of the fused select (1% slower with tile
 // groups) and launches that compute only flagged tiles take single tiles.
@@ -597,6 +600,10 @@ hipError_t launch_indexer_t(const void* q, int64_t q_row_stride, const void* k,
                                                  h_i, accumulate, opt, (nq + 63) / 64,
                                                  n_pool_tiles, 1, stream);
   }
+  if (!FP8 && !opt.cand)  // bf16 scores: 16-row tiles (four waves per SIMD), 2-3% faster
+    return launch_indexer_nb<D, 1, FP8, false>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
+                                               scores, ld, q_start, nq, n_pools, h_i, accumulate,
+                                               opt, tiles16, n_pool_tiles, 1, stream);
   return launch_indexer_nb<D, 2, FP8, false>(q, q_row_stride, k, k_row_stride, w, w_row_stride,
                                              scores, ld, q_start, nq, n_pools, h_i, accumulate,
                                              opt, tiles32, n_pool_tiles, 1, stream);
