@@ -362,7 +362,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         };
         if constexpr ((MULTI && NB > 1) || FP8) {
           // All pool blocks advance together, one contraction step at a time (the step's
-          // query fragments live only through it).
+          // query fragments live only through it).  On fp8 every MFMA of the pass issues
+          // before the first epilogue value is read (scheduling fences): left to itself the
+          // compiler reuses three accumulator sets and waits on each MFMA's result right after
+          // the next one issues; grouped, a wave's MFMAs run back to back while the other
+          // waves' epilogues fill the SIMD's VALU (2-3% faster on the 256k fp8 workload; with
+          // four column blocks the 16 live accumulators would cost a wave per SIMD).
+          float wv[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) wv[nb] = w_lds[jj * kBQ + nb * 16 + r16];
+          if constexpr (FP8 && NB <= 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ks = 0; ks < kKS; ++ks) {
             Frag qf[NB];
@@ -375,12 +384,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
                 acc[mb][nb] = mfma_frag<FP8>(kf[mb][ks], qf[nb],
                                              ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
           }
+          if constexpr (FP8 && NB <= 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float wv = w_lds[jj * kBQ + nb * 16 + r16];
+          for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) head_epilogue(mb, nb, wv);
-          }
+            for (int nb = 0; nb < NB; ++nb) head_epilogue(mb, nb, wv[nb]);
         } else {
           // bf16, single tiles and 16-row tile groups: pool blocks in pairs.  A pair's
           // products finish after its own MFMAs (2 NB independent chains), so its ReLU +
