@@ -78,15 +78,16 @@ def test_indexer_fp8_bit_exact(gpu, h_i):
     _check_scores(scores, ref, rows, wl.n_pools)
 
 
-@pytest.mark.parametrize("d_i", [128, 256])
-def test_indexer_fp8_scaled_and_general_tiles(gpu, d_i):
-    """e4m3 query tiles whose head weights are all positive powers of two take the kernel
-    that folds the weight into the MFMA's B scale; the others the general epilogue.  One call
-    mixing both (a 3.0 weight, a zero weight, negative weights in some 32-row tiles) must be
-    bit-exact against the oracle on every row, the ragged last tile included."""
-    say("case: indexer fp8 scaled/general tiles, d_i=%d" % d_i)
-    rng = np.random.default_rng(17 + d_i)
-    nq, p, h_i, q_start = 200, 900, 8, 3000
+@pytest.mark.parametrize("d_i,h_i", [(128, 8), (256, 8), (128, 12), (256, 12)])
+def test_indexer_fp8_mixed_weights(gpu, d_i, h_i):
+    """e4m3 indexer with head weights of every kind in one call: tiles whose weights are
+    all positive powers of two and tiles with a 3.0 weight, a zero weight or negative
+    weights must all be bit-exact against the oracle on every row, the ragged last tile
+    included.  At d_i = 128 eight heads take the 64-row tiles of few-head launches; the
+    other cases take 32-row tiles, whose MFMAs issue as one group per head."""
+    say("case: indexer fp8 mixed weights, d_i=%d, %d heads" % (d_i, h_i))
+    rng = np.random.default_rng(17 + d_i + h_i)
+    nq, p, q_start = 200, 900, 3000
     x = rng.integers(-8, 9, size=(nq, h_i, d_i)).astype(np.float32)
     y = rng.integers(-8, 9, size=(p, d_i)).astype(np.float32)
     q = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).to(gpu)
