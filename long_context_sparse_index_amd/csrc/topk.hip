@@ -6,19 +6,28 @@
 // first among equal scores, -1 in the slots beyond the visible count.
 //
 // One 1024-thread block per query row.  Scores are mapped to order-preserving 32-bit keys.
-// Pass A streams the row into an LDS histogram of the top 12 key bits, and a block-wide
-// suffix scan picks the bin holding the k-th largest key.  When that bin is taken whole or
-// holds at most 4096 keys (the usual case), pass B streams the row once more and moves the
-// keys above the bin to the winner list and the bin's keys to an LDS candidate list, both
-// through LDS slot counters, so pass B needs no block-wide synchronisation.  The remaining
-// 20 key bits are then resolved over the candidates alone (two 10-bit digit histograms);
-// if more candidates share the exact threshold key than slots remain, a select on the
-// pool index among them keeps the lowest pools, so ties resolve exactly as a stable full
-// sort.  A bin too large for the list is resolved over the row itself, followed by a
-// pool-ordered pass (block-wide prefix scans) that gives the remaining slots to the
-// threshold-equal keys of lowest pool.  The k winners are sorted on (~key, pool) by a
-// bitonic network held in registers (lane shuffles within a wave, LDS across waves) and
-// written out.  Rows with no more visible pools than k sort the whole prefix.
+// Every path ends in one LDS list of at most 4096 (~key, pool) entries that holds the row's
+// k winners; the list is sorted whole and its first k entries written:
+//   * rows of at most 4096 visible pools list every visible pool;
+//   * rows of up to 16384 pools are read once into registers; their smallest and largest
+//     keys set the window of a 12-bit LDS histogram, a block-wide suffix scan picks the bin
+//     holding the k-th largest key, and the keys in that bin or above it are listed;
+//   * longer rows histogram a 1/16 sample of the row the same way, take the lower edge of
+//     the bin holding the sample key ranked 1.5 k (scaled to the sample), and stream the
+//     row once more, listing every score at or above that edge.
+// Appends reserve their slots with one LDS atomic per wave.  The list is sorted by rank:
+// entries go to 2048 buckets by a monotone map of their key, a block scan of the bucket
+// counts gives each bucket's start, and each entry's position is its bucket's start plus
+// the number of its bucket's entries that precede it in (~key, pool) order; a bucket of
+// more than 64 entries (heavy ties) sends the list to a bitonic network in registers
+// instead.  Ties therefore resolve as a stable full sort.  A row whose list does not hold
+// k..4096 entries is marked in its first output slot and selected by a second, persistent
+// launch with the exact two-pass select: a 12-bit histogram of the whole row picks the bin
+// of the k-th largest key; the bin's keys are listed, or, when it holds more than the list,
+// its remaining bits are resolved over the row by 10-bit digit histograms and a
+// pool-ordered pass (block-wide prefix scans) gives the last slots to the threshold-equal
+// keys of lowest pool.  A third form selects from the candidate lists of the fused
+// indexer select.
 
 #include <type_traits>
 
