@@ -684,16 +684,17 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       if (u < nu)  // uniform
         x[u] = *reinterpret_cast<const f32x4*>(srow + 4 * min(index4(u), n4 - 1));
     // Launches whose sampled rows take at most three listing rounds load the first round
-    // here, so that its latency hides behind the threshold work (62 instead of 42 VGPRs,
-    // still eight waves per SIMD; 3-7% faster on such launches).  Longer rows keep the plain
-    // kernel: its smaller register set measured faster there.
+    // here, so that its latency hides behind the threshold work, and keep the next round's
+    // loads in flight while one round is listed (62 instead of 42 VGPRs, still eight waves
+    // per SIMD; 4-9% faster on such launches).  Longer rows keep the plain kernel, which
+    // measured 1-2% faster there.
     constexpr bool kAhead = MODE == kTopkScoreRowsAhead && !kWhole;
-    f32x4 first[kListF4];
+    f32x4 ahead[kListF4];  // the listing round loaded ahead
     if constexpr (kAhead) {
 #pragma unroll
       for (int u = 0; u < kListF4; ++u) {
         const int i4 = u * kTopkThreads + tid;
-        first[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+        ahead[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -814,14 +815,24 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(
       uint32_t* const buf32 = reinterpret_cast<uint32_t*>(buf);
       for (int base = 0; base < n4; base += kListF4 * kTopkThreads) {
         f32x4 v[kListF4];
+        if constexpr (kAhead) {
 #pragma unroll
-        for (int u = 0; u < kListF4; ++u) {
-          const int i4 = base + u * kTopkThreads + tid;
-          if (kAhead && base == 0)
-            v[u] = first[u];
-          else
+          for (int u = 0; u < kListF4; ++u) v[u] = ahead[u];
+          if (base + kListF4 * kTopkThreads < n4) {  // uniform: the next round's loads
+#pragma unroll
+            for (int u = 0; u < kListF4; ++u) {
+              const int i4 = base + (kListF4 + u) * kTopkThreads + tid;
+              ahead[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < kListF4; ++u) {
+            const int i4 = base + u * kTopkThreads + tid;
             v[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(srow + 4 * i4)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
         // Visible elements of this lane's group in round u (4 when the wave's round is whole).
         auto n_visible = [&](int u) {
